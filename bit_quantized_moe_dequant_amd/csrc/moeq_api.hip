@@ -1,0 +1,431 @@
+// C ABI of the library: argument checks, workspace layout and kernel dispatch.
+// Everything here runs on the host; kernels are launched asynchronously on the
+// caller's stream and nothing is allocated or synchronised on the forward path.
+#include <string.h>
+#include <math.h>
+
+#include "moeq.h"
+#include "moeq_kernels.h"
+
+using namespace moeq;
+
+namespace {
+
+constexpr int PREFILL_MIN_T = 128;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int block_k(int fmt) {
+  switch (fmt) {
+    case MOEQ_FMT_MXFP4: return 32;
+    case MOEQ_FMT_NVFP4: return 16;
+    case MOEQ_FMT_Q2_K: return 256;
+    case MOEQ_FMT_IQ2_XXS: return 256;
+    case MOEQ_FMT_FP8_B128: return 128;
+  }
+  return 0;
+}
+
+size_t plane_bytes(int fmt, int rows, int cols, int plane) {
+  int bk = block_k(fmt);
+  if (bk == 0 || rows <= 0 || cols <= 0 || cols % bk || (plane != 0 && plane != 1)) return 0;
+  size_t n = (size_t)rows * cols;
+  switch (fmt) {
+    case MOEQ_FMT_MXFP4: return plane == 0 ? n / 2 : n / 32;
+    case MOEQ_FMT_NVFP4: return plane == 0 ? n / 2 : n / 16;
+    case MOEQ_FMT_Q2_K: return (size_t)rows * (cols / 256) * (plane == 0 ? 64 : 20);
+    case MOEQ_FMT_IQ2_XXS: return (size_t)rows * (cols / 256) * (plane == 0 ? 64 : 2);
+    case MOEQ_FMT_FP8_B128:
+      if (rows % 128) return 0;
+      return plane == 0 ? n : (size_t)(rows / 128) * (cols / 128);
+  }
+  return 0;
+}
+
+WeightRef ref_of(const moeq_weight& w) {
+  WeightRef r;
+  r.data = (const uint8_t*)w.data;
+  r.scales = (const uint8_t*)w.scales;
+  r.estride = w.expert_stride;
+  r.sestride = w.scale_expert_stride;
+  r.scale2 = w.fmt == MOEQ_FMT_NVFP4 ? w.scale2 : nullptr;
+  return r;
+}
+
+// Checks a weight descriptor; gemv = the tensor is used by the GEMV kernels.
+int check_weight(const moeq_weight* w, bool gemv) {
+  if (!w) return MOEQ_E_INVAL;
+  if (block_k(w->fmt) == 0) return MOEQ_E_FMT;
+  if (w->n_experts <= 0) return MOEQ_E_INVAL;
+  size_t p0 = plane_bytes(w->fmt, w->rows, w->cols, 0), p1 = plane_bytes(w->fmt, w->rows, w->cols, 1);
+  if (p0 == 0 || p1 == 0) return MOEQ_E_SHAPE;
+  if (w->cols % weights_per_chunk(w->fmt)) return MOEQ_E_SHAPE;
+  if (gemv) {
+    int lpr, cpl;
+    if (!chunk_geometry(w->fmt, w->cols, &lpr, &cpl)) return MOEQ_E_SHAPE;
+  }
+  if (!w->data || !w->scales) return MOEQ_E_INVAL;
+  if (!aligned(w->data, 16) || !aligned(w->scales, 4)) return MOEQ_E_ALIGN;
+  if (w->n_experts > 1) {
+    if (w->expert_stride < p0 || w->scale_expert_stride < p1) return MOEQ_E_INVAL;
+    if (w->expert_stride % 16 || w->scale_expert_stride % 4) return MOEQ_E_ALIGN;
+  }
+  if (w->fmt == MOEQ_FMT_NVFP4 && (!w->scale2 || !aligned(w->scale2, 4))) return MOEQ_E_INVAL;
+  if (w->fmt == MOEQ_FMT_IQ2_XXS && !w->grid) return MOEQ_E_INVAL;
+  return MOEQ_OK;
+}
+
+int check_layer(const moeq_layer* L) {
+  if (!L) return MOEQ_E_INVAL;
+  if (L->hidden <= 0 || L->inter <= 0 || L->n_experts <= 0 || L->top_k < 1 || L->top_k > 16) return MOEQ_E_INVAL;
+  if (L->n_experts > 1024) return MOEQ_E_SHAPE;
+  int rc;
+  if ((rc = check_weight(&L->gate, true)) || (rc = check_weight(&L->up, true)) || (rc = check_weight(&L->down, true)))
+    return rc;
+  if (L->gate.rows != L->inter || L->gate.cols != L->hidden) return MOEQ_E_SHAPE;
+  if (L->up.rows != L->inter || L->up.cols != L->hidden) return MOEQ_E_SHAPE;
+  if (L->down.rows != L->hidden || L->down.cols != L->inter) return MOEQ_E_SHAPE;
+  if (L->gate.fmt != L->up.fmt) return MOEQ_E_FMT;
+  if (L->gate.n_experts < L->n_experts || L->up.n_experts < L->n_experts || L->down.n_experts < L->n_experts)
+    return MOEQ_E_INVAL;
+  // h is read as fp32 in 16-byte pieces; x as bf16 in 16-byte pieces
+  if (L->inter % 4 || L->hidden % 8) return MOEQ_E_SHAPE;
+  return MOEQ_OK;
+}
+
+bool prefill_path(const moeq_layer* L, int T) {
+  return T >= PREFILL_MIN_T && L->gate.fmt == MOEQ_FMT_MXFP4 && L->up.fmt == MOEQ_FMT_MXFP4 &&
+         L->down.fmt == MOEQ_FMT_MXFP4;
+}
+
+struct WsLayout {
+  size_t route, h, partial, xq, xs, hq, hs, total;
+};
+
+WsLayout ws_layout(const moeq_layer* L, int T) {
+  const size_t P = (size_t)T * L->top_k;
+  WsLayout w;
+  size_t off = 256;  // header: device error word at 0
+  w.route = off;
+  off += align_up(RouteView::words(L->n_experts, (int)P) * 4, 256);
+  w.h = off;
+  off += align_up(P * L->inter * 4, 256);
+  w.partial = off;
+  off += T > 1 ? align_up(P * L->hidden * 4, 256) : 0;
+  w.xq = w.xs = w.hq = w.hs = 0;
+  if (prefill_path(L, T)) {
+    w.xq = off;
+    off += align_up((size_t)T * L->hidden, 256);
+    w.xs = off;
+    off += align_up((size_t)T * L->hidden / 32, 256);
+    w.hq = off;
+    off += align_up(P * L->inter, 256);
+    w.hs = off;
+    off += align_up(P * L->inter / 32, 256);
+  }
+  w.total = off;
+  return w;
+}
+
+int check_ws(const moeq_layer* L, int T, void* ws, size_t ws_bytes) {
+  if (!ws) return MOEQ_E_WORKSPACE;
+  if (!aligned(ws, 256)) return MOEQ_E_ALIGN;
+  if (ws_bytes < ws_layout(L, T).total) return MOEQ_E_WORKSPACE;
+  return MOEQ_OK;
+}
+
+inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOEQ_OK : MOEQ_E_HIP; }
+inline hipStream_t S(void* s) { return (hipStream_t)s; }
+inline uint32_t* err_word(void* ws) { return (uint32_t*)ws; }
+inline RouteView route_view(const moeq_layer* L, void* ws, const WsLayout& lay) {
+  RouteView rv;
+  rv.base = (int32_t*)((uint8_t*)ws + lay.route);
+  rv.E = L->n_experts;
+  return rv;
+}
+
+GemvParams gemv_params(const moeq_layer* L, const moeq_weight& a, const moeq_weight* b, void* ws,
+                       const WsLayout& lay) {
+  GemvParams p;
+  memset(&p, 0, sizeof(p));
+  p.w[0] = ref_of(a);
+  p.w[1] = b ? ref_of(*b) : ref_of(a);
+  p.grid = a.grid;
+  p.rows = a.rows;
+  p.cols = a.cols;
+  p.n_experts = L ? L->n_experts : a.n_experts;
+  p.top_k = L ? L->top_k : 1;
+  if (ws) {
+    p.route = route_view(L, ws, lay);
+    p.err = err_word(ws);
+  }
+  return p;
+}
+
+int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
+                hipStream_t s) {
+  GemvParams p = gemv_params(L, L->gate, &L->up, ws, lay);
+  p.act = x;
+  p.ids = ids;
+  p.T = T;
+  p.out = h;
+  if (T == 1) {
+    p.mode = MODE_DIRECT;
+    return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, L->top_k, 1, s));
+  }
+  p.mode = MODE_GROUPED;
+  int slots = L->n_experts + 1;
+  if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
+  return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, 4, s));
+}
+
+int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
+             const WsLayout& lay, hipStream_t s) {
+  if (T == 1) {
+    Down1Params d;
+    memset(&d, 0, sizeof(d));
+    d.w = ref_of(L->down);
+    d.grid = L->down.grid;
+    d.rows = L->down.rows;
+    d.cols = L->down.cols;
+    d.n_experts = L->n_experts;
+    d.top_k = L->top_k;
+    d.h = h;
+    d.ids = ids;
+    d.rw = rw;
+    d.y = y;
+    d.err = err_word(ws);
+    return hip_rc(launch_down1(L->down.fmt, d, s));
+  }
+  GemvParams p = gemv_params(L, L->down, nullptr, ws, lay);
+  p.act = h;
+  p.ids = ids;
+  p.rw = rw;
+  p.T = T;
+  p.mode = MODE_GROUPED;
+  float* partial = (float*)((uint8_t*)ws + lay.partial);
+  p.out = partial;
+  int slots = L->n_experts + 1;
+  if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
+  int rc = hip_rc(launch_gemv(L->down.fmt, EPI_PARTIAL, p, slots, 2, s));
+  if (rc) return rc;
+  return hip_rc(launch_combine(partial, T, L->top_k, L->hidden, y, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moeq_abi_version(void) { return MOEQ_ABI_VERSION; }
+
+const char* moeq_status_string(int status) {
+  switch (status) {
+    case MOEQ_OK: return "ok";
+    case MOEQ_E_INVAL: return "invalid argument";
+    case MOEQ_E_FMT: return "unknown or unsupported format";
+    case MOEQ_E_ALIGN: return "pointer or stride not aligned";
+    case MOEQ_E_SHAPE: return "unsupported shape";
+    case MOEQ_E_WORKSPACE: return "workspace missing or too small";
+    case MOEQ_E_HIP: return "HIP launch or runtime error";
+    case MOEQ_E_LOSSY: return "conversion would not be exact";
+  }
+  return "unknown status";
+}
+
+size_t moeq_plane_bytes(int fmt, int rows, int cols, int plane) { return plane_bytes(fmt, rows, cols, plane); }
+
+size_t moeq_packed_bytes(int fmt, int rows, int cols) {
+  size_t a = plane_bytes(fmt, rows, cols, 0), b = plane_bytes(fmt, rows, cols, 1);
+  if (!a || !b) return 0;
+  return a + b + (fmt == MOEQ_FMT_NVFP4 ? 4 : 0);
+}
+
+int moeq_pack_ggml(int fmt, const void* blocks_host, int rows, int cols, void* data_host, void* scales_host) {
+  if (fmt != MOEQ_FMT_Q2_K && fmt != MOEQ_FMT_IQ2_XXS) return MOEQ_E_FMT;
+  if (!blocks_host || !data_host || !scales_host) return MOEQ_E_INVAL;
+  if (plane_bytes(fmt, rows, cols, 0) == 0) return MOEQ_E_SHAPE;
+  const size_t nblk = (size_t)rows * (cols / 256);
+  const uint8_t* src = (const uint8_t*)blocks_host;
+  uint8_t* d = (uint8_t*)data_host;
+  uint8_t* c = (uint8_t*)scales_host;
+  for (size_t b = 0; b < nblk; b++) {
+    if (fmt == MOEQ_FMT_Q2_K) {
+      const uint8_t* s = src + b * 84;
+      memcpy(d + b * 64, s + 16, 64);
+      memcpy(c + b * 20, s, 16);
+      memcpy(c + b * 20 + 16, s + 80, 4);
+    } else {
+      const uint8_t* s = src + b * 66;
+      memcpy(d + b * 64, s + 2, 64);
+      memcpy(c + b * 2, s, 2);
+    }
+  }
+  return MOEQ_OK;
+}
+
+int moeq_pack_ggml_device(int fmt, const void* blocks, int rows, int cols, int n, void* data, void* scales,
+                          void* stream) {
+  if (fmt != MOEQ_FMT_Q2_K && fmt != MOEQ_FMT_IQ2_XXS) return MOEQ_E_FMT;
+  if (!blocks || !data || !scales || n < 0) return MOEQ_E_INVAL;
+  if (plane_bytes(fmt, rows, cols, 0) == 0) return MOEQ_E_SHAPE;
+  if (n == 0) return MOEQ_OK;
+  return hip_rc(launch_pack(fmt, (const uint8_t*)blocks, rows, cols, n, (uint8_t*)data, (uint8_t*)scales, S(stream)));
+}
+
+int moeq_mxfp4_to_nvfp4(const uint8_t* nib_host, const uint8_t* e8m0_host, int rows, int cols, uint8_t* nib_out_host,
+                        uint8_t* e4m3_out_host, float* scale2_out_host) {
+  if (!nib_host || !e8m0_host || !nib_out_host || !e4m3_out_host || !scale2_out_host) return MOEQ_E_INVAL;
+  if (rows <= 0 || cols <= 0 || cols % 32) return MOEQ_E_SHAPE;
+  const size_t nblk = (size_t)rows * (cols / 32);
+  int emin = 255, emax = 0;
+  for (size_t i = 0; i < nblk; i++) {
+    int E = e8m0_host[i];
+    if (E == 255) return MOEQ_E_LOSSY;
+    emin = E < emin ? E : emin;
+    emax = E > emax ? E : emax;
+  }
+  if (emax - emin > 17) return MOEQ_E_LOSSY;
+  // Largest block exponent -> e4m3's largest power of two 2^8.
+  *scale2_out_host = ldexpf(1.0f, emax - 127 - 8);
+  for (size_t i = 0; i < nblk; i++) {
+    int k = (int)e8m0_host[i] - emax + 8;  // -9 .. 8
+    uint8_t code = k >= -6 ? (uint8_t)((k + 7) << 3) : (uint8_t)(1u << (k + 9));
+    e4m3_out_host[2 * i] = code;
+    e4m3_out_host[2 * i + 1] = code;
+  }
+  memcpy(nib_out_host, nib_host, (size_t)rows * cols / 2);
+  return MOEQ_OK;
+}
+
+int moeq_dequant(const moeq_weight* w, int expert, float* out, void* stream) {
+  int rc = check_weight(w, false);
+  if (rc) return rc;
+  if (expert < 0 || expert >= w->n_experts) return MOEQ_E_INVAL;
+  if (!out) return MOEQ_E_INVAL;
+  if (!aligned(out, 4)) return MOEQ_E_ALIGN;
+  return hip_rc(launch_dequant(w->fmt, ref_of(*w), w->grid, w->rows, w->cols, expert, out, S(stream)));
+}
+
+size_t moeq_workspace_bytes(const moeq_layer* L, int T) {
+  if (check_layer(L) || T < 0) return 0;
+  return ws_layout(L, T).total;
+}
+
+int moeq_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < 256) return MOEQ_E_WORKSPACE;
+  if (!aligned(ws, 256)) return MOEQ_E_ALIGN;
+  return hip_rc(launch_clear_words((uint32_t*)ws, 64, S(stream)));
+}
+
+int moeq_route(const moeq_layer* L, const int32_t* ids, int T, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0 || !ids) return MOEQ_E_INVAL;
+  if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+  if (T == 0) return MOEQ_OK;
+  WsLayout lay = ws_layout(L, T);
+  return hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_word(ws), S(stream)));
+}
+
+int moeq_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0 || !x || !ids || !h) return MOEQ_E_INVAL;
+  if (!aligned(x, 16) || !aligned(h, 16)) return MOEQ_E_ALIGN;
+  if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+  if (T == 0) return MOEQ_OK;
+  return run_gate_up(L, x, ids, T, h, ws, ws_layout(L, T), S(stream));
+}
+
+int moeq_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
+              size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0 || !h || !ids || !rw || !y) return MOEQ_E_INVAL;
+  if (!aligned(h, 16) || !aligned(y, 4)) return MOEQ_E_ALIGN;
+  if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+  if (T == 0) return MOEQ_OK;
+  return run_down(L, h, ids, rw, T, y, ws, ws_layout(L, T), S(stream));
+}
+
+int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0 || !x || !ids || !rw || !y) return MOEQ_E_INVAL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return MOEQ_E_ALIGN;
+  if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+  if (T == 0) return MOEQ_OK;
+  WsLayout lay = ws_layout(L, T);
+  hipStream_t s = S(stream);
+  float* h = (float*)((uint8_t*)ws + lay.h);
+  if (T > 1) {
+    rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_word(ws), s));
+    if (rc) return rc;
+  }
+  if ((rc = run_gate_up(L, x, ids, T, h, ws, lay, s))) return rc;
+  return run_down(L, h, ids, rw, T, y, ws, lay, s);
+}
+
+int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, const int32_t* ids, int T,
+                         float* h_f32, uint8_t* hq, uint8_t* hs, void* ws, size_t ws_bytes, void* stream) {
+  (void)L; (void)xq; (void)xs; (void)ids; (void)T; (void)h_f32; (void)hq; (void)hs; (void)ws; (void)ws_bytes;
+  (void)stream;
+  return MOEQ_E_FMT;
+}
+
+int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, const int32_t* ids, const float* rw,
+                      int T, float* y, void* ws, size_t ws_bytes, void* stream) {
+  (void)L; (void)hq; (void)hs; (void)ids; (void)rw; (void)T; (void)y; (void)ws; (void)ws_bytes; (void)stream;
+  return MOEQ_E_FMT;
+}
+
+int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y, void* stream) {
+  int rc = check_weight(w, true);
+  if (rc) return rc;
+  if (expert < 0 || expert >= w->n_experts || T < 0 || !x || !y) return MOEQ_E_INVAL;
+  if (!aligned(x, 16) || !aligned(y, 4)) return MOEQ_E_ALIGN;
+  if (w->cols % 8) return MOEQ_E_SHAPE;
+  if (T == 0) return MOEQ_OK;
+  WsLayout lay;
+  memset(&lay, 0, sizeof(lay));
+  GemvParams p = gemv_params(nullptr, *w, nullptr, nullptr, lay);
+  p.act = x;
+  p.T = T;
+  p.expert = expert;
+  p.mode = MODE_LINEAR;
+  p.out = y;
+  return hip_rc(launch_gemv(w->fmt, EPI_PLAIN, p, 1, T > 1 ? 4 : 1, S(stream)));
+}
+
+int moeq_quantize_mxfp8_bf16(const void* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream) {
+  if (!x || !q || !e8m0 || T < 0) return MOEQ_E_INVAL;
+  if (K <= 0 || K % 32) return MOEQ_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16)) return MOEQ_E_ALIGN;
+  if (T == 0) return MOEQ_OK;
+  return hip_rc(launch_quant_mxfp8(0, x, T, K, q, e8m0, S(stream)));
+}
+
+int moeq_quantize_mxfp8_f32(const float* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream) {
+  if (!x || !q || !e8m0 || T < 0) return MOEQ_E_INVAL;
+  if (K <= 0 || K % 32) return MOEQ_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16)) return MOEQ_E_ALIGN;
+  if (T == 0) return MOEQ_OK;
+  return hip_rc(launch_quant_mxfp8(1, x, T, K, q, e8m0, S(stream)));
+}
+
+int moeq_check_device_error(void* ws, void* stream, uint32_t* err_host, int clear) {
+  if (!ws || !err_host) return MOEQ_E_INVAL;
+  hipStream_t s = S(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return MOEQ_E_HIP;
+  if (hipMemcpy(err_host, ws, 4, hipMemcpyDeviceToHost) != hipSuccess) return MOEQ_E_HIP;
+  if (clear) {
+    if (launch_clear_words((uint32_t*)ws, 1, s) != hipSuccess) return MOEQ_E_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOEQ_E_HIP;
+  }
+  return MOEQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,444 @@
+// Fused dequantize + GEMV kernels for the decode path, and the dequant kernel.
+//
+// Layout of the work: every lane owns a fixed slice of the contraction axis (CPL
+// chunks of one 128-bit load each, chunks lr, lr + lpr, ... of a row, so a wave's
+// loads are contiguous), keeps the activation slice for that range in registers,
+// and walks over weight rows; `lpr` lanes share a row (lpr = 64 when a row has at
+// least 64 chunks). Partial sums are reduced across the lpr lanes with halving
+// exchanges. Weight bytes are read exactly once from HBM per token group.
+//
+// Kernels:
+//   k_gemv<..., EPI_SWIGLU>  gate and up rows of one expert together, h = silu(g) u
+//                            (REAP K180 Mixed NVFP4 card, "Why this mix?": gate/up
+//                            carry two thirds of the expert bytes in decode)
+//   k_gemv<..., EPI_PARTIAL> down rows, route-weighted, one output row per pair
+//   k_gemv<..., EPI_PLAIN>   dense linear (FP8 block-128 dense layers)
+//   k_down1                  down rows for a single token: one wave per routed
+//                            expert, top-k combine in LDS in slot order
+//   k_dequant                exact weights to fp32
+#include "moeq_device.h"
+#include "moeq_kernels.h"
+
+namespace moeq {
+
+template <int FMT>
+__device__ __forceinline__ WView expert_view(const WeightRef& w, int e, int rows, int cols) {
+  WView v;
+  v.data = w.data + (size_t)e * w.estride;
+  v.scales = w.scales + (size_t)e * w.sestride;
+  v.rows = rows;
+  v.cols = cols;
+  return v;
+}
+
+// ---------------------------------------------------------------- dequant
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant(WeightRef w, const uint8_t* grid, int rows, int cols, int expert,
+                                                 float* out) {
+  using D = Dec<FMT>;
+  const int chunks = cols / D::WPC;
+  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)rows * chunks) return;
+  int r = (int)(idx / chunks), ch = (int)(idx % chunks);
+  WView v = expert_view<FMT>(w, expert, rows, cols);
+  u32x4 q = ld16(D::chunk_ptr(v, r, ch));
+  typename D::Side s = D::side(v, r, ch);
+  float s2 = (FMT == FMT_NVFP4) ? w.scale2[expert] : 1.0f;
+  float o[D::WPC];
+  D::to_f32(q, s, s2, grid, o);
+  float* orow = out + (size_t)r * cols;
+#pragma unroll
+  for (int j = 0; j < D::WPC; j++) orow[D::out_col(ch, j)] = o[j];
+}
+
+// ---------------------------------------------------------------- GEMV
+template <int FMT, int CPL, int MT, int NMAT, int EPI, int ACT, int UB>
+__global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
+  using D = Dec<FMT>;
+  typedef typename D::Side Side;
+  constexpr int XN = XRegs<FMT, ACT>::N;
+  constexpr int XS = XRegs<FMT, ACT>::NS;
+  constexpr int NV = UB * MT;
+  __shared__ Iq2Lds lds_tab[FMT == FMT_IQ2_XXS ? 1 : 1];
+  (void)lds_tab;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = blockIdx.y;
+  const int lpr = P.lpr;
+  const int rw_rows = 64 / lpr;  // rows per wave step
+  const int lr = lane & (lpr - 1);
+  const int rsub = lane / lpr;
+
+  // Resolve the expert and its pairs.
+  int e, M, pstart = 0;
+  if (P.mode == MODE_DIRECT) {
+    e = P.ids[slot];
+    M = 1;
+  } else if (P.mode == MODE_GROUPED) {
+    if (slot >= P.route.n_slots()[0]) return;
+    e = P.route.slots()[slot];
+    pstart = P.route.offsets()[e];
+    M = P.route.offsets()[e + 1] - pstart;
+  } else {
+    e = P.expert;
+    M = P.T;
+  }
+
+  const int tile_r0 = blockIdx.x * P.rows_per_wg;
+  const int wr0 = tile_r0 + wave * (P.U * rw_rows);
+  const bool bad = (e < 0 || e >= P.n_experts);
+  if (bad) {
+    // Out-of-range expert id: its pairs contribute nothing. Zero their outputs.
+    if (P.mode == MODE_DIRECT && threadIdx.x == 0 && blockIdx.x == 0) atomicOr(P.err, 1u);
+    if (EPI != EPI_PLAIN) {
+      for (int m = 0; m < M; m++) {
+        int pair = (P.mode == MODE_DIRECT) ? slot : P.route.perm()[pstart + m];
+        for (int r = tile_r0 + threadIdx.x; r < tile_r0 + P.rows_per_wg && r < P.rows; r += 256)
+          P.out[(size_t)pair * P.rows + r] = 0.f;
+      }
+    }
+    return;
+  }
+
+  if constexpr (FMT == FMT_IQ2_XXS) {
+    iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 256);
+    __syncthreads();
+  }
+
+  WView W[NMAT];
+#pragma unroll
+  for (int mt = 0; mt < NMAT; mt++) W[mt] = expert_view<FMT>(P.w[mt], e, P.rows, P.cols);
+  float s2[NMAT];
+#pragma unroll
+  for (int mt = 0; mt < NMAT; mt++) s2[mt] = (FMT == FMT_NVFP4) ? P.w[mt].scale2[e] : 1.0f;
+
+  for (int m0 = 0; m0 < M; m0 += MT) {
+    uint32_t x[MT][CPL][XN];
+    float xs[MT][CPL][XS];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) {
+      const int m = m0 + mi;
+      if (m < M) {
+        int pair = (P.mode == MODE_DIRECT) ? slot : (P.mode == MODE_GROUPED ? P.route.perm()[pstart + m] : m);
+        const void* row;
+        if (ACT == ACT_BF16) {
+          int tok = (P.mode == MODE_LINEAR) ? m : pair / P.top_k;
+          row = reinterpret_cast<const uint16_t*>(P.act) + (size_t)tok * P.cols;
+        } else {
+          row = reinterpret_cast<const float*>(P.act) + (size_t)pair * P.cols;
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          if (lr + lpr * c < P.chunks) {
+            D::template load_x<ACT>(row, lr + lpr * c, x[mi][c], xs[mi][c]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < XN; j++) x[mi][c][j] = 0u;
+#pragma unroll
+            for (int j = 0; j < XS; j++) xs[mi][c][j] = 0.f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+#pragma unroll
+          for (int j = 0; j < XN; j++) x[mi][c][j] = 0u;
+#pragma unroll
+          for (int j = 0; j < XS; j++) xs[mi][c][j] = 0.f;
+        }
+      }
+    }
+
+    for (int u0 = 0; u0 < P.U; u0 += UB) {
+      u32x4 q[NMAT][UB][CPL];
+      Side sd[NMAT][UB][CPL];
+#pragma unroll
+      for (int mt = 0; mt < NMAT; mt++)
+#pragma unroll
+        for (int ub = 0; ub < UB; ub++) {
+          const int r = wr0 + (u0 + ub) * rw_rows + rsub;
+#pragma unroll
+          for (int c = 0; c < CPL; c++) {
+            if (r < P.rows && lr + lpr * c < P.chunks) {
+              q[mt][ub][c] = ld16(D::chunk_ptr(W[mt], r, lr + lpr * c));
+              sd[mt][ub][c] = D::side(W[mt], r, lr + lpr * c);
+            } else {
+              q[mt][ub][c] = u32x4{0u, 0u, 0u, 0u};
+              sd[mt][ub][c] = Side{};
+            }
+          }
+        }
+      float acc[NMAT][NV];
+#pragma unroll
+      for (int mt = 0; mt < NMAT; mt++)
+#pragma unroll
+        for (int ub = 0; ub < UB; ub++)
+#pragma unroll
+          for (int mi = 0; mi < MT; mi++) {
+            float a = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+              a = D::template dot<ACT>(q[mt][ub][c], sd[mt][ub][c], x[mi][c], xs[mi][c], a, &lds_tab[0]);
+            acc[mt][ub * MT + mi] = a;
+          }
+#pragma unroll
+      for (int mt = 0; mt < NMAT; mt++) group_reduce<NV>(acc[mt], lpr, lane);
+
+      // Lane holds value indices vi0 + i, i < nf.
+      const int nf = NV >= lpr ? NV / lpr : 1;
+      const bool writer = NV >= lpr ? true : ((lr % (lpr / NV)) == 0);
+      const int vi0 = (lr * NV) / lpr;
+      if (writer) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+          if (i < nf) {
+            const int vi = vi0 + i;
+            const int ub = vi / MT, mi = vi % MT;
+            const int r = wr0 + (u0 + ub) * rw_rows + rsub;
+            const int m = m0 + mi;
+            if (r < P.rows && m < M) {
+              int pair = (P.mode == MODE_DIRECT) ? slot : (P.mode == MODE_GROUPED ? P.route.perm()[pstart + m] : m);
+              float v;
+              if (EPI == EPI_SWIGLU) {
+                v = silu_mul(acc[0][i] * s2[0], acc[NMAT - 1][i] * s2[NMAT - 1]);
+              } else if (EPI == EPI_PARTIAL) {
+                v = acc[0][i] * s2[0] * P.rw[pair];
+              } else {
+                v = acc[0][i] * s2[0];
+              }
+              P.out[(size_t)pair * P.rows + r] = v;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down for one token
+template <int FMT, int CPL, int UB>
+__global__ __launch_bounds__(1024) void k_down1(Down1Params P) {
+  using D = Dec<FMT>;
+  typedef typename D::Side Side;
+  constexpr int XN = XRegs<FMT, ACT_F32>::N;
+  constexpr int XS = XRegs<FMT, ACT_F32>::NS;
+  __shared__ Iq2Lds lds_tab[1];
+  __shared__ float red[16][64];
+
+  const int lane = threadIdx.x & 63;
+  const int k = threadIdx.x >> 6;  // slot handled by this wave
+  const int lpr = P.lpr;
+  const int rw_rows = 64 / lpr;
+  const int lr = lane & (lpr - 1);
+  const int rsub = lane / lpr;
+  const int tile_r0 = blockIdx.x * P.rows_per_wg;
+
+  if constexpr (FMT == FMT_IQ2_XXS) {
+    iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
+
+  const int e = P.ids[k];
+  const bool ok = (e >= 0 && e < P.n_experts);
+  if (!ok && lane == 0 && blockIdx.x == 0) atomicOr(P.err, 1u);
+  if (ok) {
+    WView W = expert_view<FMT>(P.w, e, P.rows, P.cols);
+    const float s2 = (FMT == FMT_NVFP4) ? P.w.scale2[e] : 1.0f;
+    const float wk = P.rw[k] * s2;
+    uint32_t x[CPL][XN];
+    float xs[CPL][XS];
+    const float* hrow = P.h + (size_t)k * P.cols;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      if (lr + lpr * c < P.chunks) {
+        D::template load_x<ACT_F32>(hrow, lr + lpr * c, x[c], xs[c]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < XN; j++) x[c][j] = 0u;
+#pragma unroll
+        for (int j = 0; j < XS; j++) xs[c][j] = 0.f;
+      }
+    }
+    for (int u0 = 0; u0 < P.U; u0 += UB) {
+      u32x4 q[UB][CPL];
+      Side sd[UB][CPL];
+#pragma unroll
+      for (int ub = 0; ub < UB; ub++) {
+        const int r = tile_r0 + (u0 + ub) * rw_rows + rsub;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          if (r < P.rows && u0 + ub < P.U && lr + lpr * c < P.chunks) {
+            q[ub][c] = ld16(D::chunk_ptr(W, r, lr + lpr * c));
+            sd[ub][c] = D::side(W, r, lr + lpr * c);
+          } else {
+            q[ub][c] = u32x4{0u, 0u, 0u, 0u};
+            sd[ub][c] = Side{};
+          }
+        }
+      }
+      float acc[UB];
+#pragma unroll
+      for (int ub = 0; ub < UB; ub++) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) a = D::template dot<ACT_F32>(q[ub][c], sd[ub][c], x[c], xs[c], a, &lds_tab[0]);
+        acc[ub] = a;
+      }
+      group_reduce<UB>(acc, lpr, lane);
+      const int nf = UB >= lpr ? UB / lpr : 1;
+      const bool writer = UB >= lpr ? true : ((lr % (lpr / UB)) == 0);
+      const int vi0 = (lr * UB) / lpr;
+      if (writer) {
+#pragma unroll
+        for (int i = 0; i < UB; i++) {
+          if (i < nf) {
+            const int ub = vi0 + i;
+            if (u0 + ub < P.U) red[k][(u0 + ub) * rw_rows + rsub] = acc[i] * wk;
+          }
+        }
+      }
+    }
+  } else {
+    for (int i = lane; i < P.rows_per_wg; i += 64) red[k][i] = 0.f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < P.rows_per_wg; i += blockDim.x) {
+    const int r = tile_r0 + i;
+    if (r < P.rows) {
+      float y = 0.f;
+      for (int kk = 0; kk < P.top_k; kk++) y += red[kk][i];
+      P.y[r] = y;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+int weights_per_chunk(int fmt) {
+  switch (fmt) {
+    case FMT_MXFP4: return 32;
+    case FMT_NVFP4: return 32;
+    case FMT_Q2_K: return 64;
+    case FMT_IQ2_XXS: return 64;
+    case FMT_FP8_B128: return 16;
+  }
+  return 0;
+}
+
+// lpr = lanes sharing a row (a power of two <= 64), cpl = chunks per lane (1, 2
+// or 4); lanes whose chunk index falls past the row end are masked.
+bool chunk_geometry(int fmt, int cols, int* lpr, int* cpl) {
+  int wpc = weights_per_chunk(fmt);
+  if (wpc == 0 || cols <= 0 || cols % wpc) return false;
+  int chunks = cols / wpc;
+  int l = 1;
+  while (l < chunks && l < 64) l <<= 1;
+  int c = (chunks + l - 1) / l;
+  if (c == 3) c = 4;
+  if (c > 4) return false;
+  *lpr = l;
+  *cpl = c;
+  return true;
+}
+
+hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int rows, int cols, int expert, float* out,
+                          hipStream_t s) {
+  int wpc = weights_per_chunk(fmt);
+  size_t n = (size_t)rows * (cols / wpc);
+  dim3 grid_dim((unsigned)((n + 255) / 256)), blk(256);
+  switch (fmt) {
+    case FMT_MXFP4: hipLaunchKernelGGL(k_dequant<FMT_MXFP4>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out); break;
+    case FMT_NVFP4: hipLaunchKernelGGL(k_dequant<FMT_NVFP4>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out); break;
+    case FMT_Q2_K: hipLaunchKernelGGL(k_dequant<FMT_Q2_K>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out); break;
+    case FMT_IQ2_XXS:
+      hipLaunchKernelGGL(k_dequant<FMT_IQ2_XXS>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out);
+      break;
+    case FMT_FP8_B128:
+      hipLaunchKernelGGL(k_dequant<FMT_FP8_B128>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int CPL>
+static hipError_t gemv_fc(int epi, const GemvParams& p, dim3 g, int mt, hipStream_t s) {
+  dim3 b(256);
+  if (epi == EPI_SWIGLU) {
+    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, 4>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, 4>), g, b, 0, s, p);
+  } else if (epi == EPI_PARTIAL) {
+    hipLaunchKernelGGL((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, 4>), g, b, 0, s, p);
+  } else {
+    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, 4>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 1, EPI_PLAIN, ACT_BF16, 4>), g, b, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t gemv_f(int epi, const GemvParams& p, int cpl, dim3 g, int mt, hipStream_t s) {
+  switch (cpl) {
+    case 1: return gemv_fc<FMT, 1>(epi, p, g, mt, s);
+    case 2: return gemv_fc<FMT, 2>(epi, p, g, mt, s);
+    case 4: return gemv_fc<FMT, 4>(epi, p, g, mt, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int mt, hipStream_t s) {
+  int lpr, cpl;
+  if (!chunk_geometry(fmt, p.cols, &lpr, &cpl)) return hipErrorInvalidValue;
+  GemvParams q = p;
+  q.lpr = lpr;
+  q.chunks = p.cols / weights_per_chunk(fmt);
+  int rw_rows = 64 / lpr;
+  q.U = 4;
+  q.rows_per_wg = 4 * q.U * rw_rows;
+  dim3 g((unsigned)((p.rows + q.rows_per_wg - 1) / q.rows_per_wg), (unsigned)n_slots);
+  switch (fmt) {
+    case FMT_MXFP4: return gemv_f<FMT_MXFP4>(epi, q, cpl, g, mt, s);
+    case FMT_NVFP4: return gemv_f<FMT_NVFP4>(epi, q, cpl, g, mt, s);
+    case FMT_Q2_K: return gemv_f<FMT_Q2_K>(epi, q, cpl, g, mt, s);
+    case FMT_IQ2_XXS: return gemv_f<FMT_IQ2_XXS>(epi, q, cpl, g, mt, s);
+    case FMT_FP8_B128: return gemv_f<FMT_FP8_B128>(epi, q, cpl, g, mt, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+static hipError_t down1_f(const Down1Params& p, int cpl, dim3 g, dim3 b, hipStream_t s) {
+  switch (cpl) {
+    case 1: hipLaunchKernelGGL((k_down1<FMT, 1, 4>), g, b, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_down1<FMT, 2, 4>), g, b, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_down1<FMT, 4, 4>), g, b, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down1(int fmt, const Down1Params& p, hipStream_t s) {
+  int lpr, cpl;
+  if (!chunk_geometry(fmt, p.cols, &lpr, &cpl)) return hipErrorInvalidValue;
+  Down1Params q = p;
+  q.lpr = lpr;
+  q.chunks = p.cols / weights_per_chunk(fmt);
+  int rw_rows = 64 / lpr;
+  q.U = 8;
+  q.rows_per_wg = q.U * rw_rows;  // <= 64 rows (red[] bound)
+  if (q.rows_per_wg > 64) {
+    q.U = 64 / rw_rows;
+    q.rows_per_wg = 64;
+  }
+  dim3 g((unsigned)((p.rows + q.rows_per_wg - 1) / q.rows_per_wg)), b((unsigned)(64 * p.top_k));
+  switch (fmt) {
+    case FMT_MXFP4: return down1_f<FMT_MXFP4>(q, cpl, g, b, s);
+    case FMT_NVFP4: return down1_f<FMT_NVFP4>(q, cpl, g, b, s);
+    case FMT_Q2_K: return down1_f<FMT_Q2_K>(q, cpl, g, b, s);
+    case FMT_IQ2_XXS: return down1_f<FMT_IQ2_XXS>(q, cpl, g, b, s);
+    case FMT_FP8_B128: return down1_f<FMT_FP8_B128>(q, cpl, g, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moeq

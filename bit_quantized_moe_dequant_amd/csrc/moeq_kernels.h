@@ -1,0 +1,77 @@
+// Kernel parameter blocks and host-side launchers shared by the kernel sources
+// and the C ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq {
+
+enum { MODE_DIRECT = 0, MODE_GROUPED = 1, MODE_LINEAR = 2 };
+enum { EPI_SWIGLU = 0, EPI_PARTIAL = 1, EPI_PLAIN = 2 };
+
+// Routing block inside the workspace (int32 words):
+//   [0]                n_slots (touched experts, plus one slot for invalid ids if any)
+//   [1, E + 2)         slot -> expert (E marks the bucket of out-of-range ids)
+//   [E + 2, 2E + 4)    bucket offsets into perm (bucket E = out-of-range ids)
+//   [2E + 4, ...)      perm: pair indices grouped by expert
+struct RouteView {
+  int32_t* base;
+  int E;
+  __host__ __device__ int32_t* n_slots() const { return base; }
+  __host__ __device__ int32_t* slots() const { return base + 1; }
+  __host__ __device__ int32_t* offsets() const { return base + E + 2; }
+  __host__ __device__ int32_t* perm() const { return base + 2 * E + 4; }
+  static size_t words(int E, int P) { return (size_t)(2 * E + 4 + P); }
+};
+
+struct WeightRef {
+  const uint8_t* data;
+  const uint8_t* scales;
+  size_t estride, sestride;
+  const float* scale2;  // NVFP4 per-expert scale_2 or nullptr
+};
+
+struct GemvParams {
+  WeightRef w[2];
+  const uint8_t* grid;  // IQ2_XXS codebook
+  int rows, cols, n_experts, lpr, chunks;
+  const void* act;      // bf16 [tokens][cols] or fp32 [pairs][cols]
+  int mode, T, top_k, expert;
+  const int32_t* ids;
+  RouteView route;
+  const float* rw;
+  float* out;
+  uint32_t* err;
+  int rows_per_wg, U;
+};
+
+struct Down1Params {
+  WeightRef w;
+  const uint8_t* grid;
+  int rows, cols, n_experts, lpr, chunks, top_k;
+  const float* h;  // fp32 [top_k][cols]
+  const int32_t* ids;
+  const float* rw;
+  float* y;
+  uint32_t* err;
+  int rows_per_wg, U;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int rows, int cols, int expert, float* out,
+                          hipStream_t s);
+hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int mt, hipStream_t s);
+hipError_t launch_down1(int fmt, const Down1Params& p, hipStream_t s);
+hipError_t launch_route(const int32_t* ids, int P, int E, RouteView rv, uint32_t* err, hipStream_t s);
+hipError_t launch_combine(const float* partial, int T, int K, int H, float* y, hipStream_t s);
+hipError_t launch_quant_mxfp8(int in_f32, const void* x, int T, int K, uint8_t* q, uint8_t* e, hipStream_t s);
+hipError_t launch_pack(int fmt, const uint8_t* blocks, int rows, int cols, int n, uint8_t* data, uint8_t* scales,
+                       hipStream_t s);
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s);
+
+// Chunk geometry: weights per 16-byte chunk; lanes per row and chunks per lane.
+int weights_per_chunk(int fmt);
+bool chunk_geometry(int fmt, int cols, int* lpr, int* cpl);
+
+}  // namespace moeq

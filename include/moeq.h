@@ -1,0 +1,211 @@
+/*
+ * moeq.h - C ABI of the MI355X (gfx950) block-quantized routed-MoE library.
+ *
+ * The library computes the routed-expert projection of a DeepSeek-V4-Flash-shaped
+ * MoE layer (DeepSeek-V4-Flash W4A16-FP8 model card, "Architecture & precision",
+ * base-model table: 256 routed experts, top-6, hidden 4096, 43 layers) with expert
+ * weights in block-quantized formats, on one GPU:
+ *
+ *   for token t routed to experts e_k with route weights w_k (k < top_k):
+ *     h_k = silu(G_e x_t) * (U_e x_t),   y_t = sum_k w_k * (D_e h_k)
+ *
+ * At decode (few tokens) this is a fused dequantize + GEMV per projection; at
+ * prefill with MXFP4 weights it is a token-grouped GEMM on the block-scaled FP4
+ * matrix instructions, with activations quantised to MXFP8 (fp4 weights times
+ * E4M3 activations: DeepSeekv4 Flash for 1x Spark forum thread, second post).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_host are host memory; every other buffer pointer is device
+ *    memory on the current HIP device, owned and allocated by the caller. The
+ *    library never allocates, frees or synchronises on the forward path and keeps
+ *    no global state; launches are asynchronous on `stream` (a hipStream_t passed
+ *    as void*, NULL = the default stream) and may be captured into a HIP graph.
+ *  - Arguments are checked on the host before any launch; a check that fails
+ *    returns a negative MOEQ_E_* code and launches nothing. MOEQ_E_HIP reports a
+ *    launch error. Faults inside kernels follow HIP semantics (reported at the
+ *    next synchronisation). Expert ids outside [0, n_experts) never cause an
+ *    out-of-bounds access: the pair is skipped (its outputs are zero) and
+ *    MOEQ_DEVERR_EXPERT_ID is set in the workspace's device error word.
+ *  - Element order: rows are output features, cols are input features (the
+ *    contraction axis); all matrices are row-major.
+ */
+#ifndef MOEQ_H_
+#define MOEQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEQ_ABI_VERSION 1
+
+/* ------------------------------------------------------------------ formats
+ * Device layout of one expert tensor [rows, cols] (the `data` and `scales`
+ * planes of moeq_weight; experts are expert_stride / scale_expert_stride bytes
+ * apart):
+ *
+ * MOEQ_FMT_MXFP4 - e2m1 elements, one e8m0 scale per 32 along cols (REAP K180
+ *   Mixed NVFP4 card, lossless MXFP4 -> NVFP4 conversion section; 4.25 bits per
+ *   weight in the 1x Spark forum thread, first post).
+ *   data: u8 [rows][cols/2], element 2j in the low nibble of byte j.
+ *   scales: u8 [rows][cols/32] e8m0 codes; weight = e2m1 * 2^(E-127), E=255 NaN.
+ * MOEQ_FMT_NVFP4 - e2m1 elements, one e4m3 scale per 16, one fp32 scale_2 per
+ *   expert tensor (same card, "Why this mix?": 4.50 bits per weight).
+ *   data: as MXFP4. scales: u8 [rows][cols/16] e4m3fn codes.
+ *   scale2: fp32 [n_experts]. weight = e2m1 * e4m3 * scale_2.
+ * MOEQ_FMT_Q2_K - ggml 256-weight superblocks, 84 bytes (2.625 bits per weight;
+ *   IQ2_XXS + Q2_K + FP8 hybrid card, format table). Stored as two planes so
+ *   every load is aligned; moeq_pack_ggml converts from the contiguous block.
+ *   data: u8 [rows][cols/256][64] = the block's qs bytes.
+ *   scales: u8 [rows][cols/256][20] = the block's 16 scale bytes, then d and
+ *   dmin (fp16, little-endian).
+ *   weight i of a superblock: j = i/16, h = i/128, r = i%128,
+ *   q = (qs[32h + r%32] >> 2*(r/32)) & 3,
+ *   w = d * (sc[j] & 15) * q - dmin * (sc[j] >> 4).
+ * MOEQ_FMT_IQ2_XXS - ggml 256-weight superblocks, 66 bytes (2.0625 bits per
+ *   weight; same table). Two planes:
+ *   data: u8 [rows][cols/256][64] = 8 sub-blocks of (u32 a0, u32 a1).
+ *   scales: fp16 d [rows][cols/256].
+ *   grid: u8 [256][8] device codebook (an input: any values 0..255).
+ *   weight 32b + 8l + j: db = d * (0.5 + (a1 >> 28)) / 4,
+ *   g = grid[(a0 >> 8l) & 255][j], c = (a1 >> 7l) & 127,
+ *   mask = c | parity(c) << 7, w = (mask >> j & 1 ? -1 : 1) * db * g.
+ * MOEQ_FMT_FP8_B128 - E4M3 weights with one UE8M0 scale per 128x128 tile (IQ2_XXS
+ *   + Q2_K + FP8 hybrid card, format table; W4A16-FP8 card, FP8 block 128x128).
+ *   data: u8 [rows][cols] e4m3fn codes. scales: u8 [rows/128][cols/128].
+ */
+#define MOEQ_FMT_MXFP4 1
+#define MOEQ_FMT_NVFP4 2
+#define MOEQ_FMT_Q2_K 3
+#define MOEQ_FMT_IQ2_XXS 4
+#define MOEQ_FMT_FP8_B128 5
+
+/* ------------------------------------------------------------------ status */
+#define MOEQ_OK 0
+#define MOEQ_E_INVAL -1     /* null pointer, negative count, bad argument */
+#define MOEQ_E_FMT -2       /* unknown format, or a format the entry point does not take */
+#define MOEQ_E_ALIGN -3     /* pointer or stride not aligned as documented */
+#define MOEQ_E_SHAPE -4     /* shape the format or the kernels cannot hold */
+#define MOEQ_E_WORKSPACE -5 /* workspace missing or smaller than moeq_workspace_bytes */
+#define MOEQ_E_HIP -6       /* a HIP call or kernel launch failed */
+#define MOEQ_E_LOSSY -7     /* MXFP4 -> NVFP4 cannot be exact (span > 17 or NaN scale) */
+
+/* Bits of the device error word (first 4 bytes of a workspace). */
+#define MOEQ_DEVERR_EXPERT_ID 1u /* an expert id was outside [0, n_experts) */
+
+/* ------------------------------------------------------------------ descriptors
+ * Read on the host only, during the call. */
+typedef struct moeq_weight {
+  int fmt;                    /* MOEQ_FMT_* */
+  int rows;                   /* output features */
+  int cols;                   /* input features */
+  int n_experts;              /* experts stored expert-major */
+  const void* data;           /* 16-byte aligned */
+  size_t expert_stride;       /* bytes between experts in data, multiple of 16 */
+  const void* scales;         /* 4-byte aligned */
+  size_t scale_expert_stride; /* bytes between experts in scales, multiple of 4 */
+  const float* scale2;        /* NVFP4: fp32 [n_experts]; else ignored */
+  const uint8_t* grid;        /* IQ2_XXS: u8 [256][8]; else ignored */
+} moeq_weight;
+
+typedef struct moeq_layer {
+  int hidden;    /* H: gate/up cols, down rows */
+  int inter;     /* I: gate/up rows, down cols */
+  int n_experts; /* E */
+  int top_k;     /* K, 1..16 */
+  moeq_weight gate, up, down;
+} moeq_layer;
+
+/* ------------------------------------------------------------------ sizes */
+int moeq_abi_version(void);
+const char* moeq_status_string(int status);
+
+/* Bytes of plane 0 (data) or plane 1 (scales) of one expert tensor [rows, cols];
+ * 0 for an invalid format, plane or shape. cols must be a multiple of the format's
+ * block: 32 MXFP4, 16 NVFP4, 256 Q2_K and IQ2_XXS, 128 FP8_B128 (rows too). */
+size_t moeq_plane_bytes(int fmt, int rows, int cols, int plane);
+
+/* Total bytes of one expert tensor, both planes plus NVFP4's 4-byte scale_2. The
+ * algorithmic bytes per weight equal the format's bits per weight / 8. */
+size_t moeq_packed_bytes(int fmt, int rows, int cols);
+
+/* ------------------------------------------------------------------ host utilities */
+
+/* Repack contiguous ggml blocks (Q2_K: 84 B, IQ2_XXS: 66 B per 256 weights, rows x
+ * cols/256 blocks row-major) into the two device planes, in host memory. */
+int moeq_pack_ggml(int fmt, const void* blocks_host, int rows, int cols, void* data_host, void* scales_host);
+
+/* Device version over n tensors stored back to back (block bytes, data and scale
+ * planes each contiguous per tensor). */
+int moeq_pack_ggml_device(int fmt, const void* blocks, int rows, int cols, int n, void* data, void* scales,
+                          void* stream);
+
+/* Lossless MXFP4 -> NVFP4 re-encode of one tensor in host memory (REAP K180 Mixed
+ * NVFP4 card, conversion section and "How It Was Built" step 3): nibbles copied,
+ * e8m0 per 32 -> e4m3 per 16 with scale_2 = 2^(Emax-135), e4m3 = 2^(E-Emax+8).
+ * MOEQ_E_LOSSY if Emax - Emin > 17 or a code is 255; outputs are then untouched. */
+int moeq_mxfp4_to_nvfp4(const uint8_t* nib_host, const uint8_t* e8m0_host, int rows, int cols, uint8_t* nib_out_host,
+                        uint8_t* e4m3_out_host, float* scale2_out_host);
+
+/* ------------------------------------------------------------------ kernels */
+
+/* Dequantise expert `expert` of w to fp32 [rows][cols]. The value is the format's
+ * exact weight rounded once to fp32 (exact for MXFP4, IQ2_XXS, FP8_B128). */
+int moeq_dequant(const moeq_weight* w, int expert, float* out, void* stream);
+
+/* Workspace bytes needed by moeq_expert_forward / the stage entry points for T
+ * tokens. The workspace must be zero-filled once before first use (or passed to
+ * moeq_workspace_init); its first 4 bytes hold the sticky device error word. */
+size_t moeq_workspace_bytes(const moeq_layer* L, int T);
+int moeq_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* y[T][H] (fp32, overwritten) of the routed layer for x[T][H] (bf16), expert ids
+ * ids[T][K] (int32) and route weights rw[T][K] (fp32, applied after down as given).
+ * Decode path (GEMV, any format) unless T >= 128 and gate, up and down are all
+ * MXFP4, in which case the W4A8 prefill path runs (x and h quantised to MXFP8).
+ * T == 0 is a no-op. x, y 16-byte aligned. */
+int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Stages of the decode path, for tests and timing (moeq_expert_forward runs them
+ * in order). moeq_route groups the T*K (token, slot) pairs by expert into the
+ * workspace (needed before the other two when T > 1). moeq_gate_up writes
+ * h[T][K][I] (fp32) = silu(G x) * (U x) per pair. moeq_down writes y[T][H]. */
+int moeq_route(const moeq_layer* L, const int32_t* ids, int T, void* ws, size_t ws_bytes, void* stream);
+int moeq_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, size_t ws_bytes,
+                 void* stream);
+int moeq_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* Stages of the W4A8 prefill path (MXFP4 weights only; moeq_route first).
+ * moeq_prefill_gate_up: xq/xs = MXFP8 x (codes u8 [T][H], e8m0 u8 [T][H/32]) ->
+ *   hq/hs = MXFP8 h (codes u8 [T*K][I], e8m0 u8 [T*K][I/32]); h_f32 (may be NULL)
+ *   receives h before quantisation, fp32 [T*K][I].
+ * moeq_prefill_down: hq/hs -> y[T][H]. */
+int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, const int32_t* ids, int T,
+                         float* h_f32, uint8_t* hq, uint8_t* hs, void* ws, size_t ws_bytes, void* stream);
+int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, const int32_t* ids, const float* rw,
+                      int T, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Dense block-quantized linear y[T][rows] = W_expert x[T][cols] (fp32 out). Any
+ * format; FP8_B128 is the dense-layer format (IQ2_XXS + Q2_K + FP8 hybrid card). */
+int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y, void* stream);
+
+/* MXFP8 quantisation of rows of K values (K a multiple of 32): per 32 consecutive
+ * values, e8m0 code E = clamp(e + 127, 0, 254) with 2^e the smallest power of two
+ * keeping max|v| / 2^e <= 448 (e = p-9 if the frexp mantissa of max|v| is <= 0.875,
+ * else p-8; all-zero block: E = 0, codes 0); codes = E4M3FN round-to-nearest-even of
+ * v / 2^(E-127), saturating, sign kept. _bf16 takes bf16 input, _f32 fp32. */
+int moeq_quantize_mxfp8_bf16(const void* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream);
+int moeq_quantize_mxfp8_f32(const float* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream);
+
+/* Synchronise `stream`, then read (and with clear != 0, zero) the device error word. */
+int moeq_check_device_error(void* ws, void* stream, uint32_t* err_host, int clear);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H_ */

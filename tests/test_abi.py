@@ -1,0 +1,134 @@
+"""CPU tests of the C ABI library: it loads, exports every declared symbol,
+rejects bad arguments before touching the GPU, and its host utilities agree with
+the oracle."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import bit_quantized_moe_dequant_amd as mq
+from bit_quantized_moe_dequant_amd import synth
+from oracle import convert, formats
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moeq.h", "moeq_synth.h")]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mq.library_path()), reason="libmoeq.so not built")
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mq.library_path())
+    names = []
+    for h in HEADERS:
+        names += mq.header_functions(h)
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert missing == []
+    assert mq._lib().moeq_abi_version() == 1
+
+
+def test_status_strings():
+    lib = mq._lib()
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert lib.moeq_status_string(code) != b"unknown status"
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
+def test_packed_bytes_match_oracle(fmt):
+    for rows, cols in [(2048, 4096), (4096, 2048), (128, 256), (512, 1024)]:
+        assert mq.packed_bytes(fmt, rows, cols) == formats.packed_bytes(fmt, rows, cols)
+    assert mq.packed_bytes(fmt, 128, 100) == 0
+
+
+def _fake_weight(fmt=1, rows=256, cols=512, data=0x10000, scales=0x20000, n=1):
+    return mq.MoeqWeight(fmt, rows, cols, n, data, 1 << 20, scales, 1 << 20, 0x30000, 0x40000)
+
+
+def test_validation_rejects_before_launch():
+    lib = mq._lib()
+    out = ctypes.c_void_p(0x50000)
+    w = _fake_weight(fmt=99)
+    assert lib.moeq_dequant(ctypes.byref(w), 0, out, None) == -2
+    w = _fake_weight(data=0x10004)
+    assert lib.moeq_dequant(ctypes.byref(w), 0, out, None) == -3
+    w = _fake_weight(cols=500)
+    assert lib.moeq_dequant(ctypes.byref(w), 0, out, None) == -4
+    w = _fake_weight()
+    assert lib.moeq_dequant(ctypes.byref(w), 1, out, None) == -1      # expert out of range
+    assert lib.moeq_dequant(ctypes.byref(w), 0, None, None) == -1
+    w = _fake_weight(fmt=4)
+    w.grid = 0
+    assert lib.moeq_dequant(ctypes.byref(w), 0, out, None) == -1      # IQ2_XXS needs a codebook
+
+
+def _fake_layer(H=1024, I=512, E=8, K=2):
+    g = _fake_weight(1, I, H, n=E)
+    u = _fake_weight(1, I, H, n=E)
+    d = _fake_weight(1, H, I, n=E)
+    return mq.MoeqLayer(H, I, E, K, g, u, d)
+
+
+def test_workspace_and_forward_validation():
+    lib = mq._lib()
+    L = _fake_layer()
+    n1 = lib.moeq_workspace_bytes(ctypes.byref(L), 1)
+    n64 = lib.moeq_workspace_bytes(ctypes.byref(L), 64)
+    assert 0 < n1 < n64
+    ws = ctypes.c_void_p(0x100000)
+    x, ids, rw, y = (ctypes.c_void_p(a) for a in (0x200000, 0x300000, 0x400000, 0x500000))
+    assert lib.moeq_expert_forward(ctypes.byref(L), x, ids, rw, 1, y, ws, n1 - 1, None) == -5
+    assert lib.moeq_expert_forward(ctypes.byref(L), x, ids, rw, -1, y, ws, n1, None) == -1
+    assert lib.moeq_expert_forward(ctypes.byref(L), ctypes.c_void_p(0x200002), ids, rw, 1, y, ws, n1, None) == -3
+    assert lib.moeq_expert_forward(ctypes.byref(L), x, ids, rw, 0, y, ws, n1, None) == 0   # T = 0: no-op
+    bad = _fake_layer()
+    bad.down.rows = 512                                                                    # down must be [H, I]
+    assert lib.moeq_expert_forward(ctypes.byref(bad), x, ids, rw, 1, y, ws, n1, None) == -4
+    bad = _fake_layer(K=17)
+    assert lib.moeq_workspace_bytes(ctypes.byref(bad), 1) == 0
+
+
+def test_quantize_validation():
+    lib = mq._lib()
+    p = ctypes.c_void_p(0x100000)
+    assert lib.moeq_quantize_mxfp8_bf16(p, 4, 48, p, p, None) == -4
+    assert lib.moeq_quantize_mxfp8_f32(p, 4, 64, ctypes.c_void_p(0x100004), p, None) == -3
+    assert lib.moeq_quantize_mxfp8_f32(p, 0, 64, p, p, None) == 0
+
+
+@pytest.mark.parametrize("fmt,bs", [(3, 84), (4, 66)])
+def test_pack_ggml_host(fmt, bs):
+    rows, cols = 3, 512
+    blocks = synth.raw_bytes(7, fmt, 0, rows * (cols // 256) * bs)
+    d, s = mq.pack_ggml(fmt, blocks, rows, cols)
+    b = blocks.reshape(-1, bs)
+    if fmt == 3:
+        assert np.array_equal(d.reshape(-1, 64), b[:, 16:80])
+        assert np.array_equal(s.reshape(-1, 20)[:, :16], b[:, :16])
+        assert np.array_equal(s.reshape(-1, 20)[:, 16:], b[:, 80:84])
+    else:
+        assert np.array_equal(d.reshape(-1, 64), b[:, 2:66])
+        assert np.array_equal(s.reshape(-1, 2), b[:, 0:2])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mxfp4_to_nvfp4_host_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    rows, cols = 8, 128
+    nib = rng.integers(0, 256, rows * cols // 2, dtype=np.uint8)
+    lo = int(rng.integers(0, 230))
+    e8 = rng.integers(lo, lo + 18, rows * cols // 32).astype(np.uint8)
+    n2, e4, s2 = mq.mxfp4_to_nvfp4(nib, e8, rows, cols)
+    o_n, o_e4, o_s2 = convert.mxfp4_to_nvfp4(nib, e8, rows, cols)
+    assert n2.tobytes() == o_n.tobytes()
+    assert e4.tobytes() == o_e4.reshape(-1).tobytes()
+    assert np.float32(s2) == o_s2
+
+
+def test_mxfp4_to_nvfp4_host_refuses_lossy():
+    nib = np.zeros(32, np.uint8)
+    with pytest.raises(mq.MoeqError) as ei:
+        mq.mxfp4_to_nvfp4(nib, np.array([10, 28], np.uint8), 1, 64)
+    assert ei.value.status == -7
+    with pytest.raises(mq.MoeqError):
+        mq.mxfp4_to_nvfp4(np.zeros(16, np.uint8), np.array([255], np.uint8), 1, 32)
