@@ -141,10 +141,10 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const void* x, int T, int K
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       u32x4 w = ld16(p + 4 * i);
-      v[4 * i + 0] = __builtin_bit_cast(float, w[0]);
-      v[4 * i + 1] = __builtin_bit_cast(float, w[1]);
-      v[4 * i + 2] = __builtin_bit_cast(float, w[2]);
-      v[4 * i + 3] = __builtin_bit_cast(float, w[3]);
+      v[4 * i + 0] = u2f(w[0]);
+      v[4 * i + 1] = u2f(w[1]);
+      v[4 * i + 2] = u2f(w[2]);
+      v[4 * i + 3] = u2f(w[3]);
     }
   } else {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + b * 32;
@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const void* x, int T, int K
       u32x4 w = ld16(p + 8 * i);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        v[8 * i + 2 * j] = __builtin_bit_cast(float, w[j] << 16);
-        v[8 * i + 2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
+        v[8 * i + 2 * j] = u2f(w[j] << 16);
+        v[8 * i + 2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
       }
     }
   }

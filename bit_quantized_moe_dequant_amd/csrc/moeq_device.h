@@ -25,6 +25,11 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Scalar bit casts. Always cast through these: applied directly to an element of
+// an ext_vector_type value, __builtin_bit_cast reads the vector's first element.
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), acc,
                                          false);
@@ -92,8 +97,8 @@ template <> struct Act<ACT_F32> {
 #pragma unroll
     for (int i = 0; i < N / 4; i++) {
       u32x4 v = ld16(p + 4 * i);
-      split_pair(__builtin_bit_cast(float, v[0]), __builtin_bit_cast(float, v[1]), r[2 * i], r[N / 2 + 2 * i]);
-      split_pair(__builtin_bit_cast(float, v[2]), __builtin_bit_cast(float, v[3]), r[2 * i + 1], r[N / 2 + 2 * i + 1]);
+      split_pair(u2f(v[0]), u2f(v[1]), r[2 * i], r[N / 2 + 2 * i]);
+      split_pair(u2f(v[2]), u2f(v[3]), r[2 * i + 1], r[N / 2 + 2 * i + 1]);
     }
   }
   __device__ static float val(const void* row, int k) { return reinterpret_cast<const float*>(row)[k]; }
@@ -284,8 +289,8 @@ template <> struct Dec<FMT_Q2_K> {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           u32x4 v = ld16(f + 4 * i);
-          float x0 = __builtin_bit_cast(float, v[0]), x1 = __builtin_bit_cast(float, v[1]);
-          float x2 = __builtin_bit_cast(float, v[2]), x3 = __builtin_bit_cast(float, v[3]);
+          float x0 = u2f(v[0]), x1 = u2f(v[1]);
+          float x2 = u2f(v[2]), x3 = u2f(v[3]);
           split_pair(x0, x2, x[8 * p + 2 * i], x[32 + 8 * p + 2 * i]);
           split_pair(x1, x3, x[8 * p + 2 * i + 1], x[32 + 8 * p + 2 * i + 1]);
           s += (x0 + x1) + (x2 + x3);
