@@ -18,7 +18,7 @@
 namespace moeq {
 
 enum { FMT_MXFP4 = 1, FMT_NVFP4 = 2, FMT_Q2_K = 3, FMT_IQ2_XXS = 4, FMT_FP8_B128 = 5 };
-enum { ACT_BF16 = 0, ACT_F32 = 1 };
+enum { ACT_BF16 = 0, ACT_F32 = 1, ACT_F32_COHERENT = 2 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -65,6 +65,18 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Four fp32 values read with agent-scope loads: coherent across the XCDs' L2s
+// (never a stale L2 copy), for data another work-group has just published.
+__device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  u32x4 v;
+  v[0] = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v[1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v[2] = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v[3] = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
 // -------------------------------------------------------------------------
 // Activation slices. XR<ACT>(n) = registers for n weights.
 template <int ACT> struct Act;
@@ -104,11 +116,27 @@ template <> struct Act<ACT_F32> {
   __device__ static float val(const void* row, int k) { return reinterpret_cast<const float*>(row)[k]; }
 };
 
+template <> struct Act<ACT_F32_COHERENT> {
+  static constexpr int PER_PAIR = 2;
+  // n contiguous fp32 values -> n/2 hi pairs then n/2 lo pairs
+  template <int N>
+  __device__ static void load(const void* row, int k0, uint32_t* r) {
+    const float* p = reinterpret_cast<const float*>(row) + k0;
+#pragma unroll
+    for (int i = 0; i < N / 4; i++) {
+      u32x4 v = ld16_coherent(p + 4 * i);
+      split_pair(u2f(v[0]), u2f(v[1]), r[2 * i], r[N / 2 + 2 * i]);
+      split_pair(u2f(v[2]), u2f(v[3]), r[2 * i + 1], r[N / 2 + 2 * i + 1]);
+    }
+  }
+  __device__ static float val(const void* row, int k) { return reinterpret_cast<const float*>(row)[k]; }
+};
+
 // dot of a bf16 weight pair with activation pair j of a slice of N weights
 template <int ACT, int N>
 __device__ __forceinline__ float dotp(uint32_t w, const uint32_t* x, int j, float acc) {
   acc = dot2(w, x[j], acc);
-  if (ACT == ACT_F32) acc = dot2(w, x[N / 2 + j], acc);
+  if (ACT != ACT_BF16) acc = dot2(w, x[N / 2 + j], acc);
   return acc;
 }
 
@@ -288,7 +316,7 @@ template <> struct Dec<FMT_Q2_K> {
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          u32x4 v = ld16(f + 4 * i);
+          u32x4 v = ACT == ACT_F32_COHERENT ? ld16_coherent(f + 4 * i) : ld16(f + 4 * i);
           float x0 = u2f(v[0]), x1 = u2f(v[1]);
           float x2 = u2f(v[2]), x3 = u2f(v[3]);
           split_pair(x0, x2, x[8 * p + 2 * i], x[32 + 8 * p + 2 * i]);
@@ -465,7 +493,7 @@ template <> struct Dec<FMT_FP8_B128> {
 
 // Registers of one chunk's activation slice for a format and activation kind.
 template <int FMT, int ACT> struct XRegs {
-  static constexpr int N = Dec<FMT>::WPC / 2 * (ACT == ACT_F32 ? 2 : 1);
+  static constexpr int N = Dec<FMT>::WPC / 2 * (ACT != ACT_BF16 ? 2 : 1);
   static constexpr int NS = (FMT == FMT_Q2_K) ? 4 : 1;
 };
 
@@ -496,7 +524,7 @@ __device__ __forceinline__ void group_reduce(float* v, int lpr, int lane) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   // silu(g) * u = g / (1 + e^-g) * u
-  return g / (1.0f + __expf(-g)) * u;
+  return __fdividef(g, 1.0f + __expf(-g)) * u;
 }
 
 }  // namespace moeq

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void k_dequant(WeightRef w, const uint8_t* gri
 }
 
 // ---------------------------------------------------------------- GEMV
-template <int FMT, int CPL, int MT, int NMAT, int EPI, int ACT, int UB>
+template <int FMT, int CPL, int MT, int NMAT, int EPI, int ACT, int UB, int NB>
 __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
   using D = Dec<FMT>;
   typedef typename D::Side Side;
@@ -150,7 +150,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
       }
     }
 
-    for (int u0 = 0; u0 < P.U; u0 += UB) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const int u0 = nb * UB;
       u32x4 q[NMAT][UB][CPL];
       Side sd[NMAT][UB][CPL];
 #pragma unroll
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
 }
 
 // ---------------------------------------------------------------- down for one token
-template <int FMT, int CPL, int UB>
+template <int FMT, int CPL, int UB, int NB>
 __global__ __launch_bounds__(1024) void k_down1(Down1Params P) {
   using D = Dec<FMT>;
   typedef typename D::Side Side;
@@ -260,7 +262,9 @@ __global__ __launch_bounds__(1024) void k_down1(Down1Params P) {
         for (int j = 0; j < XS; j++) xs[c][j] = 0.f;
       }
     }
-    for (int u0 = 0; u0 < P.U; u0 += UB) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const int u0 = nb * UB;
       u32x4 q[UB][CPL];
       Side sd[UB][CPL];
 #pragma unroll
@@ -361,17 +365,26 @@ hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int 
   return hipGetLastError();
 }
 
+#ifndef MOEQ_GEMV_NB
+#define MOEQ_GEMV_NB 1  // row batches of 4 per wave (gate/up, linear, grouped down)
+#endif
+#ifndef MOEQ_DOWN1_NB
+#define MOEQ_DOWN1_NB 2  // row batches of 4 per wave (single-token down)
+#endif
+constexpr int GEMV_UB = 4, GEMV_NB = MOEQ_GEMV_NB, DOWN1_UB = 4, DOWN1_NB = MOEQ_DOWN1_NB;
+
 template <int FMT, int CPL>
 static hipError_t gemv_fc(int epi, const GemvParams& p, dim3 g, int mt, hipStream_t s) {
   dim3 b(256);
+  constexpr int UB = GEMV_UB, NB = GEMV_NB;
   if (epi == EPI_SWIGLU) {
-    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, 4>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, 4>), g, b, 0, s, p);
+    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, 0, s, p);
   } else if (epi == EPI_PARTIAL) {
-    hipLaunchKernelGGL((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, 4>), g, b, 0, s, p);
+    hipLaunchKernelGGL((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, 0, s, p);
   } else {
-    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, 4>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 1, EPI_PLAIN, ACT_BF16, 4>), g, b, 0, s, p);
+    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -393,7 +406,7 @@ hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int m
   q.lpr = lpr;
   q.chunks = p.cols / weights_per_chunk(fmt);
   int rw_rows = 64 / lpr;
-  q.U = 4;
+  q.U = GEMV_UB * GEMV_NB;
   q.rows_per_wg = 4 * q.U * rw_rows;
   dim3 g((unsigned)((p.rows + q.rows_per_wg - 1) / q.rows_per_wg), (unsigned)n_slots);
   switch (fmt) {
@@ -408,10 +421,11 @@ hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int m
 
 template <int FMT>
 static hipError_t down1_f(const Down1Params& p, int cpl, dim3 g, dim3 b, hipStream_t s) {
+  constexpr int UB = DOWN1_UB, NB = DOWN1_NB;
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((k_down1<FMT, 1, 4>), g, b, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_down1<FMT, 2, 4>), g, b, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_down1<FMT, 4, 4>), g, b, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_down1<FMT, 1, UB, NB>), g, b, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_down1<FMT, 2, UB, NB>), g, b, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_down1<FMT, 4, UB, NB>), g, b, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -424,12 +438,9 @@ hipError_t launch_down1(int fmt, const Down1Params& p, hipStream_t s) {
   q.lpr = lpr;
   q.chunks = p.cols / weights_per_chunk(fmt);
   int rw_rows = 64 / lpr;
-  q.U = 8;
-  q.rows_per_wg = q.U * rw_rows;  // <= 64 rows (red[] bound)
-  if (q.rows_per_wg > 64) {
-    q.U = 64 / rw_rows;
-    q.rows_per_wg = 64;
-  }
+  q.U = DOWN1_UB * DOWN1_NB;
+  if (q.U * rw_rows > 64) q.U = 64 / rw_rows;  // red[] holds 64 rows
+  q.rows_per_wg = q.U * rw_rows;
   dim3 g((unsigned)((p.rows + q.rows_per_wg - 1) / q.rows_per_wg)), b((unsigned)(64 * p.top_k));
   switch (fmt) {
     case FMT_MXFP4: return down1_f<FMT_MXFP4>(q, cpl, g, b, s);
