@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE dequant path on one MI355X.
+
+Metric: routed-MoE layer weight-stream GB/s (and us/layer) at bs=1 decode, on the
+DeepSeek-V4-Flash-shaped MXFP4 layer (hidden 4096, 256 experts, intermediate
+2048, top-6; gate, up and down in MXFP4). One step = one pass of the decode hot
+path (gate/up dequant-GEMV with SwiGLU, down dequant-GEMV with the top-6
+route-weighted combine) for one token, with a fresh uniform top-6 of the 256
+experts per step (no expert repeats within 42 steps, so the weights stream from
+HBM rather than from the 256 MB last-level cache). Weights are seeded synthetic
+packed blocks resident in HBM before the timed region. Steps are captured in a
+HIP graph and replayed, so the host's launch cost does not pace the GPU.
+
+Printed: one JSON line with the metric, a `roofline` object for the dominant
+kernel (the gate/up dequant-GEMV, timed with HIP events on its stream) and a
+`cpu_baseline` object (the CPU oracle timed on a bounded sample of the same
+workload on this host).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources a traffic measurement belongs to."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_quantized_moe_dequant_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None if absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, ids, rw, x_bits, budget_s: float):
+    """The CPU oracle (exact decode + float64 layer) on the first steps of the same
+    routing sequence, until the time budget is spent."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import formats, moe
+    from bit_quantized_moe_dequant_amd import workloads
+
+    spec = wl.spec
+    per_step_bytes = None
+    done, spent = 0, 0.0
+    while spent < budget_s and done < ids.shape[0]:
+        e_list = [int(e) for e in ids[done]]
+        planes = {(p, e): workloads.host_source_planes(spec, p, e) for p in range(3) for e in e_list}
+        t0 = time.perf_counter()
+
+        def weight(p, e):
+            fmt, rows, cols = spec.proj(p)
+            return formats.dequant(fmt, planes[(p, e)], rows, cols)
+
+        moe.moe_layer(x_bits, ids[done:done + 1], rw[done:done + 1], moe.CachedWeights(weight))
+        spent += time.perf_counter() - t0
+        done += 1
+        if per_step_bytes is None:
+            per_step_bytes = sum(formats.packed_bytes(*spec.proj(p)) for p in range(3)) * spec.top_k
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {
+        "value": round(per_step_bytes * done / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(max(blas) if blas else 1),
+        "kind": "oracle",
+        "sample": (f"{done} bs=1 decode steps of the same workload and routing sequence "
+                   f"({spent:.1f} s): exact decode of the 6 routed experts' MXFP4 gate/up/down "
+                   f"(numpy, one thread) and the float64 layer (BLAS threads = cores); "
+                   f"host has {len(os.sched_getaffinity(0))} cores"),
+        "us_per_layer": round(spent / done * 1e6, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mxfp4_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)")
+
+    import torch
+
+    import bit_quantized_moe_dequant_amd as mq
+    from bit_quantized_moe_dequant_amd import synth, workloads
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "copies": 3}))
+        return
+    wl = workloads.WORKLOADS[args.workload]
+    spec = wl.spec
+    K, W = args.steps, args.warmup
+    log(f"workload {wl.name}: building layer ({spec.n_experts} experts) on the device")
+    layer = workloads.build_layer(mq, spec)
+    torch.cuda.synchronize()
+
+    ids, rw = synth.cold_routing_sequence(spec.seed, W + K, spec.n_experts, spec.top_k)
+    x_bits = workloads.activations(wl, 1)
+    ids_t = torch.from_numpy(ids).cuda()
+    rw_t = torch.from_numpy(rw).cuda()
+    x_t = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.empty((1, spec.hidden), dtype=torch.float32, device="cuda")
+    h = torch.empty((1, spec.top_k, spec.inter), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(1)
+    step_bytes = spec.top_k * layer.expert_bytes()
+    gu_bytes = spec.top_k * (layer.gate.algorithmic_bytes() + layer.up.algorithmic_bytes())
+
+    def step(i):
+        mq.expert_forward(layer, x_t, ids_t[i:i + 1], rw_t[i:i + 1], y=y, ws=ws)
+
+    # warmup (eager), then capture the timed steps into one graph
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"capturing {K} steps")
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(W + i)
+    torch.cuda.synchronize()
+    graph.replay()                                   # first replay uploads the graph
+    torch.cuda.synchronize()
+
+    # timed region: K steps
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = wall_s * 1e3 / K
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{K} steps: wall {wall_s * 1e3:.2f} ms, events {gpu_ms:.2f} ms -> {ms_per_step * 1e3:.2f} us/layer")
+
+    # Dominant kernel: the gate/up dequant-GEMV, timed in the same regime as the
+    # steps (a graph of K launches over the same routing sequence, replayed on its
+    # capture stream, bracketed by HIP events on that stream). Inside a graph the
+    # launches run back to back, so the average per launch is the kernel's time.
+    graph_gu = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph_gu, stream=cap):
+            for i in range(K):
+                mq.gate_up(layer, x_t, ids_t[W + i:W + i + 1], h=h, ws=ws)
+        graph_gu.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(cap)
+        graph_gu.replay()
+        g1.record(cap)
+    torch.cuda.synchronize()
+    gu_us = g0.elapsed_time(g1) * 1e3 / K
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    traffic = measured_traffic(wl.name)
+    err = mq.check_device_error(ws)
+    if err:
+        sys.exit(f"device error word {err:#x}")
+
+    out = {
+        "metric": "routed-MoE layer weight-stream GB/s (% of HBM peak) + us/layer, bs=1 decode",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": "DeepSeek-V4-Flash-shaped routed-MoE layer, bs=1 decode: hidden 4096, "
+                           "256 experts, intermediate 2048, top-6, MXFP4 gate/up/down (e2m1 + e8m0/32)",
+            "tokens_per_step": 1,
+            "weight_bytes_per_step": step_bytes,
+            "routing": "uniform top-6 per step, no expert repeated within 42 steps (cold)",
+            "launch": "HIP graph of the timed steps",
+            "parallelism": "single GPU",
+        },
+        "us_per_layer": round(ms_per_step * 1e3, 3),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "moe_tokens_per_s_43_layers": round(1e3 / (ms_per_step * 43), 1),
+        "roofline": {
+            "kernel": "gate/up fused dequant-GEMV + SwiGLU",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "launch_us": round(gu_us, 3),
+            "algorithmic_bytes_per_launch": gu_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(wl, ids[W:], rw[W:], x_bits, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

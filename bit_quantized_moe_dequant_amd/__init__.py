@@ -64,6 +64,7 @@ _SIGS = {
     "moeq_route": (_i, [ctypes.POINTER(MoeqLayer), _vp, _i, _vp, _sz, _vp]),
     "moeq_gate_up": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "moeq_down": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
+    "moeq_gate_up_timed": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _i, _vp, _vp, _sz, _vp, _vp, _vp]),
     "moeq_prefill_gate_up": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moeq_prefill_down": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "moeq_linear": (_i, [ctypes.POINTER(MoeqWeight), _i, _vp, _i, _vp, _vp]),
@@ -259,6 +260,23 @@ def gate_up(layer: Layer, x, ids, h=None, ws=None):
     L = layer.struct()
     _check("moeq_gate_up", _lib().moeq_gate_up(ctypes.byref(L), _ptr(x), _ptr(ids), T, _ptr(h), _ptr(ws), ws.numel(),
                                                 _stream_ptr()))
+    return h
+
+
+def gate_up_timed(layer: Layer, x, ids, start, stop, h=None, ws=None):
+    """gate_up with torch.cuda.Event objects (enable_timing=True, already recorded
+    once) bracketing the kernel's own execution."""
+    torch = _torch()
+    T = x.shape[0]
+    if h is None:
+        h = torch.empty((T, layer.top_k, layer.inter), dtype=torch.float32, device="cuda")
+    if ws is None:
+        ws = layer.workspace(T)
+    L = layer.struct()
+    _check("moeq_gate_up_timed", _lib().moeq_gate_up_timed(ctypes.byref(L), _ptr(x), _ptr(ids), T, _ptr(h), _ptr(ws),
+                                                            ws.numel(), _stream_ptr(),
+                                                            ctypes.c_void_p(start.cuda_event),
+                                                            ctypes.c_void_p(stop.cuda_event)))
     return h
 
 

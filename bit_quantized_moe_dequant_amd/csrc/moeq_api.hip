@@ -170,7 +170,7 @@ GemvParams gemv_params(const moeq_layer* L, const moeq_weight& a, const moeq_wei
 }
 
 int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
-                hipStream_t s) {
+                hipStream_t s, const LaunchEvents* ev = nullptr) {
   GemvParams p = gemv_params(L, L->gate, &L->up, ws, lay);
   p.act = x;
   p.ids = ids;
@@ -178,12 +178,12 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
   p.out = h;
   if (T == 1) {
     p.mode = MODE_DIRECT;
-    return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, L->top_k, 1, s));
+    return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, L->top_k, 1, s, ev));
   }
   p.mode = MODE_GROUPED;
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
-  return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, 4, s));
+  return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, 4, s, ev));
 }
 
 int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
@@ -343,6 +343,18 @@ int moeq_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, 
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
   if (T == 0) return MOEQ_OK;
   return run_gate_up(L, x, ids, T, h, ws, ws_layout(L, T), S(stream));
+}
+
+int moeq_gate_up_timed(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws,
+                       size_t ws_bytes, void* stream, void* start_event, void* stop_event) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0 || !x || !ids || !h) return MOEQ_E_INVAL;
+  if (!aligned(x, 16) || !aligned(h, 16)) return MOEQ_E_ALIGN;
+  if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+  if (T == 0) return MOEQ_OK;
+  LaunchEvents ev{(hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return run_gate_up(L, x, ids, T, h, ws, ws_layout(L, T), S(stream), &ev);
 }
 
 int moeq_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,

@@ -16,6 +16,8 @@
 //   k_down1                  down rows for a single token: one wave per routed
 //                            expert, top-k combine in LDS in slot order
 //   k_dequant                exact weights to fp32
+#include <hip/hip_ext.h>
+
 #include "moeq_device.h"
 #include "moeq_kernels.h"
 
@@ -373,33 +375,43 @@ hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int 
 #endif
 constexpr int GEMV_UB = 4, GEMV_NB = MOEQ_GEMV_NB, DOWN1_UB = 4, DOWN1_NB = MOEQ_DOWN1_NB;
 
+// Launch with hipExtLaunchKernelGGL when timing events are given: the events
+// then bracket the kernel's execution itself, not the queue around it.
+#define MOEQ_LAUNCH(K, g, b, s, ev, p)                                                \
+  do {                                                                                \
+    if (ev) hipExtLaunchKernelGGL(K, g, b, 0, s, (ev)->start, (ev)->stop, 0, p);       \
+    else hipLaunchKernelGGL(K, g, b, 0, s, p);                                        \
+  } while (0)
+
 template <int FMT, int CPL>
-static hipError_t gemv_fc(int epi, const GemvParams& p, dim3 g, int mt, hipStream_t s) {
+static hipError_t gemv_fc(int epi, const GemvParams& p, dim3 g, int mt, hipStream_t s, const LaunchEvents* ev) {
   dim3 b(256);
   constexpr int UB = GEMV_UB, NB = GEMV_NB;
   if (epi == EPI_SWIGLU) {
-    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, 0, s, p);
+    if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
+    else MOEQ_LAUNCH((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
   } else if (epi == EPI_PARTIAL) {
-    hipLaunchKernelGGL((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, 0, s, p);
+    MOEQ_LAUNCH((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
   } else {
-    if (mt == 1) hipLaunchKernelGGL((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<FMT, CPL, 4, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, 0, s, p);
+    if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
+    else MOEQ_LAUNCH((k_gemv<FMT, CPL, 4, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
   }
   return hipGetLastError();
 }
 
 template <int FMT>
-static hipError_t gemv_f(int epi, const GemvParams& p, int cpl, dim3 g, int mt, hipStream_t s) {
+static hipError_t gemv_f(int epi, const GemvParams& p, int cpl, dim3 g, int mt, hipStream_t s,
+                         const LaunchEvents* ev) {
   switch (cpl) {
-    case 1: return gemv_fc<FMT, 1>(epi, p, g, mt, s);
-    case 2: return gemv_fc<FMT, 2>(epi, p, g, mt, s);
-    case 4: return gemv_fc<FMT, 4>(epi, p, g, mt, s);
+    case 1: return gemv_fc<FMT, 1>(epi, p, g, mt, s, ev);
+    case 2: return gemv_fc<FMT, 2>(epi, p, g, mt, s, ev);
+    case 4: return gemv_fc<FMT, 4>(epi, p, g, mt, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int mt, hipStream_t s) {
+hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int mt, hipStream_t s,
+                       const LaunchEvents* ev) {
   int lpr, cpl;
   if (!chunk_geometry(fmt, p.cols, &lpr, &cpl)) return hipErrorInvalidValue;
   GemvParams q = p;
@@ -410,11 +422,11 @@ hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int m
   q.rows_per_wg = 4 * q.U * rw_rows;
   dim3 g((unsigned)((p.rows + q.rows_per_wg - 1) / q.rows_per_wg), (unsigned)n_slots);
   switch (fmt) {
-    case FMT_MXFP4: return gemv_f<FMT_MXFP4>(epi, q, cpl, g, mt, s);
-    case FMT_NVFP4: return gemv_f<FMT_NVFP4>(epi, q, cpl, g, mt, s);
-    case FMT_Q2_K: return gemv_f<FMT_Q2_K>(epi, q, cpl, g, mt, s);
-    case FMT_IQ2_XXS: return gemv_f<FMT_IQ2_XXS>(epi, q, cpl, g, mt, s);
-    case FMT_FP8_B128: return gemv_f<FMT_FP8_B128>(epi, q, cpl, g, mt, s);
+    case FMT_MXFP4: return gemv_f<FMT_MXFP4>(epi, q, cpl, g, mt, s, ev);
+    case FMT_NVFP4: return gemv_f<FMT_NVFP4>(epi, q, cpl, g, mt, s, ev);
+    case FMT_Q2_K: return gemv_f<FMT_Q2_K>(epi, q, cpl, g, mt, s, ev);
+    case FMT_IQ2_XXS: return gemv_f<FMT_IQ2_XXS>(epi, q, cpl, g, mt, s, ev);
+    case FMT_FP8_B128: return gemv_f<FMT_FP8_B128>(epi, q, cpl, g, mt, s, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -81,7 +81,12 @@ struct FusedParams {
 // Launchers (return hipError_t of the launch).
 hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int rows, int cols, int expert, float* out,
                           hipStream_t s);
-hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int mt, hipStream_t s);
+// start/stop (hipEvent_t, may be null): recorded at the kernel's own start and end.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int mt, hipStream_t s,
+                       const LaunchEvents* ev = nullptr);
 hipError_t launch_down1(int fmt, const Down1Params& p, hipStream_t s);
 hipError_t launch_route(const int32_t* ids, int P, int E, RouteView rv, uint32_t* err, hipStream_t s);
 hipError_t launch_combine(const float* partial, int T, int K, int H, float* y, hipStream_t s);

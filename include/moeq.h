@@ -180,6 +180,12 @@ int moeq_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, 
 int moeq_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
               size_t ws_bytes, void* stream);
 
+/* moeq_gate_up with its kernel launched so that start_event / stop_event (two
+ * hipEvent_t created with timing, passed as void*) record the kernel's own start
+ * and end, for timing that excludes queue gaps. Same arguments and outputs. */
+int moeq_gate_up_timed(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws,
+                       size_t ws_bytes, void* stream, void* start_event, void* stop_event);
+
 /* Stages of the W4A8 prefill path (MXFP4 weights only; moeq_route first).
  * moeq_prefill_gate_up: xq/xs = MXFP8 x (codes u8 [T][H], e8m0 u8 [T][H/32]) ->
  *   hq/hs = MXFP8 h (codes u8 [T*K][I], e8m0 u8 [T*K][I/32]); h_f32 (may be NULL)
