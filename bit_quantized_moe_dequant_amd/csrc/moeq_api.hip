@@ -219,6 +219,56 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
   return hip_rc(launch_combine(partial, T, L->top_k, L->hidden, y, s));
 }
 
+int check_prefill(const moeq_layer* L) {
+  if (L->gate.fmt != MOEQ_FMT_MXFP4 || L->up.fmt != MOEQ_FMT_MXFP4 || L->down.fmt != MOEQ_FMT_MXFP4) return MOEQ_E_FMT;
+  if (L->hidden % 64 || L->inter % 64 || L->hidden % 128 || L->inter % 128) return MOEQ_E_SHAPE;
+  return MOEQ_OK;
+}
+
+int run_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, int T, float* h_f32,
+                               uint8_t* hq, uint8_t* hs, void* ws, const WsLayout& lay, hipStream_t s) {
+  PrefillParams p;
+  memset(&p, 0, sizeof(p));
+  p.w[0] = ref_of(L->gate);
+  p.w[1] = ref_of(L->up);
+  p.rows = L->inter;
+  p.cols = L->hidden;
+  p.n_experts = L->n_experts;
+  p.top_k = L->top_k;
+  p.aq = xq;
+  p.as = xs;
+  p.route = route_view(L, ws, lay);
+  p.h_f32 = h_f32;
+  p.hq = hq;
+  p.hs = hs;
+  int slots = L->n_experts + 1;
+  if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
+  return hip_rc(launch_prefill(true, p, slots, s));
+}
+
+int run_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, const float* rw, int T, float* y,
+                            void* ws, const WsLayout& lay, hipStream_t s) {
+  PrefillParams p;
+  memset(&p, 0, sizeof(p));
+  p.w[0] = ref_of(L->down);
+  p.w[1] = p.w[0];
+  p.rows = L->hidden;
+  p.cols = L->inter;
+  p.n_experts = L->n_experts;
+  p.top_k = L->top_k;
+  p.aq = hq;
+  p.as = hs;
+  p.route = route_view(L, ws, lay);
+  p.rw = rw;
+  float* partial = (float*)((uint8_t*)ws + lay.partial);
+  p.partial = partial;
+  int slots = L->n_experts + 1;
+  if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
+  int rc = hip_rc(launch_prefill(false, p, slots, s));
+  if (rc) return rc;
+  return hip_rc(launch_combine(partial, T, L->top_k, L->hidden, y, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,6 +433,15 @@ int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, 
     rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_word(ws), s));
     if (rc) return rc;
   }
+  if (prefill_path(L, T) && check_prefill(L) == MOEQ_OK) {
+    uint8_t* xq = (uint8_t*)ws + lay.xq;
+    uint8_t* xs = (uint8_t*)ws + lay.xs;
+    uint8_t* hq = (uint8_t*)ws + lay.hq;
+    uint8_t* hs = (uint8_t*)ws + lay.hs;
+    if ((rc = hip_rc(launch_quant_mxfp8(0, x, T, L->hidden, xq, xs, s)))) return rc;
+    if ((rc = run_prefill_gate_up(L, xq, xs, T, nullptr, hq, hs, ws, lay, s))) return rc;
+    return run_prefill_down(L, hq, hs, rw, T, y, ws, lay, s);
+  }
   if (kOneLaunchLayer && T == 1 && fused1_supported(L->gate.fmt, L->down.fmt, L->hidden, L->inter, L->top_k)) {
     FusedParams f;
     memset(&f, 0, sizeof(f));
@@ -410,15 +469,27 @@ int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, 
 
 int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, const int32_t* ids, int T,
                          float* h_f32, uint8_t* hq, uint8_t* hs, void* ws, size_t ws_bytes, void* stream) {
-  (void)L; (void)xq; (void)xs; (void)ids; (void)T; (void)h_f32; (void)hq; (void)hs; (void)ws; (void)ws_bytes;
-  (void)stream;
-  return MOEQ_E_FMT;
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_prefill(L))) return rc;
+  if (T < 0 || !xq || !xs || !ids || !hq || !hs) return MOEQ_E_INVAL;
+  if (!aligned(xq, 16) || (h_f32 && !aligned(h_f32, 4))) return MOEQ_E_ALIGN;
+  if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+  if (T == 0) return MOEQ_OK;
+  return run_prefill_gate_up(L, xq, xs, T, h_f32, hq, hs, ws, ws_layout(L, T), S(stream));
 }
 
 int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, const int32_t* ids, const float* rw,
                       int T, float* y, void* ws, size_t ws_bytes, void* stream) {
-  (void)L; (void)hq; (void)hs; (void)ids; (void)rw; (void)T; (void)y; (void)ws; (void)ws_bytes; (void)stream;
-  return MOEQ_E_FMT;
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_prefill(L))) return rc;
+  if (T < 0 || !hq || !hs || !ids || !rw || !y) return MOEQ_E_INVAL;
+  if (!aligned(hq, 16) || !aligned(y, 4)) return MOEQ_E_ALIGN;
+  if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+  if (T == 0) return MOEQ_OK;
+  if (T < 2) return MOEQ_E_SHAPE;  // the combine buffer exists for T > 1
+  return run_prefill_down(L, hq, hs, rw, T, y, ws, ws_layout(L, T), S(stream));
 }
 
 int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y, void* stream) {

@@ -78,6 +78,20 @@ struct FusedParams {
   uint32_t spin_limit;
 };
 
+struct PrefillParams {
+  WeightRef w[2];        // gate/up pass: gate, up; down pass: down (w[0])
+  int rows, cols;        // weight shape: N x K
+  int n_experts, top_k;
+  const uint8_t* aq;     // A codes [*][cols]: xq rows indexed by token (gate/up) or hq rows by pair (down)
+  const uint8_t* as;     // A e8m0 [*][cols/32]
+  RouteView route;
+  const float* rw;
+  float* h_f32;          // gate/up: optional fp32 h [pairs][rows]
+  uint8_t* hq;           // gate/up: MXFP8 h codes [pairs][rows]
+  uint8_t* hs;           // gate/up: e8m0 [pairs][rows/32]
+  float* partial;        // down: [pairs][rows]
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int rows, int cols, int expert, float* out,
                           hipStream_t s);
@@ -96,6 +110,7 @@ hipError_t launch_pack(int fmt, const uint8_t* blocks, int rows, int cols, int n
 hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s);
 bool fused1_supported(int fg, int fd, int hidden, int inter, int top_k);
 hipError_t launch_fused1(int fg, int fd, const FusedParams& p, hipStream_t s);
+hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int n_slots, hipStream_t s);
 
 // Chunk geometry: weights per 16-byte chunk; lanes per row and chunks per lane.
 int weights_per_chunk(int fmt);
