@@ -34,6 +34,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published peak
+# Dense MFMA peak for an FP8 operand (v_mfma_scale_f32_32x32x64_f8f6f4 runs at the
+# FP8 rate unless both operands are FP6/FP4): 5.0 PFLOP/s on MI355X.
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -105,10 +108,186 @@ def cpu_baseline(wl, ids, rw, x_bits, budget_s: float):
     }
 
 
+def cpu_baseline_prefill(wl, ids, rw, x_bits, budget_s: float):
+    """The CPU oracle on the prefill workload, expert by expert (bounded memory):
+    exact decode of expert e's three MXFP4 matrices, then the W4A8 chain for the
+    tokens routed to e (MXFP8 x, h, MXFP8 h, route-weighted down partials)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import formats, moe, mxfp8
+    from bit_quantized_moe_dequant_amd import workloads
+
+    spec = wl.spec
+    X = (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    xq, xs = mxfp8.quantize(X)
+    pairs = experts = 0
+    spent = 0.0
+    for e in range(spec.n_experts):    # id order: hashed routing makes loads unrelated to ids
+        if spent >= budget_s:
+            break
+        planes = [workloads.host_source_planes(spec, p, e) for p in range(3)]
+        tok, slot = np.nonzero(ids == e)
+        t0 = time.perf_counter()
+        w = [formats.dequant(spec.proj(p)[0], planes[p], *spec.proj(p)[1:]) for p in range(3)]
+
+        def weight(p, _e, w=w):
+            return w[p]
+
+        sub = np.full((tok.size, 1), e, np.int32)
+        h = moe.prefill_h(xq[tok], xs[tok], sub, weight).reshape(tok.size, -1)
+        hq, hs = mxfp8.quantize(h)
+        moe.prefill_y(hq, hs, sub, rw[tok, slot].reshape(-1, 1), weight)
+        spent += time.perf_counter() - t0
+        pairs += tok.size
+        experts += 1
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    per_expert = sum(formats.packed_bytes(*spec.proj(p)) for p in range(3))
+    return {
+        "value": round(pairs / spec.top_k / spent, 2),
+        "unit": "tokens/s",
+        "cores": int(max(blas) if blas else 1),
+        "kind": "oracle",
+        "sample": (f"{experts} of {spec.n_experts} experts (in id order, {pairs} of {ids.size} token-expert "
+                   f"pairs, {spent:.1f} s): exact MXFP4 decode (numpy, one thread) and the float64 W4A8 "
+                   f"chain (BLAS threads = cores); tokens/s = pairs / top_k / s; "
+                   f"host has {len(os.sched_getaffinity(0))} cores"),
+        "weight_GBps": round(per_expert * experts / spent / 1e9, 4),
+    }
+
+
+def run_prefill(args, wl):
+    """The prefill workload: one step = one MoE layer over T prompt tokens (MXFP8
+    quantisation of x, routing, the W4A8 gate/up and down grouped GEMMs, combine)."""
+    import torch
+
+    import bit_quantized_moe_dequant_amd as mq
+    from bit_quantized_moe_dequant_amd import workloads
+
+    spec = wl.spec
+    T = wl.token_counts[0]
+    K, W = args.steps, args.warmup
+    log(f"workload {wl.name}: building layer ({spec.n_experts} experts) on the device")
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = workloads.routing(wl, T)
+    x_bits = workloads.activations(wl, T)
+    loads = np.bincount(ids.reshape(-1), minlength=spec.n_experts)
+    touched = int((loads > 0).sum())
+    P = T * spec.top_k
+    ids_t = torch.from_numpy(ids).cuda()
+    rw_t = torch.from_numpy(rw).cuda()
+    x_t = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.empty((T, spec.hidden), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(T)
+    step_bytes = touched * layer.expert_bytes()
+    gu_bytes = touched * (layer.gate.algorithmic_bytes() + layer.up.algorithmic_bytes())
+    gu_flop = 2 * P * 2 * spec.inter * spec.hidden
+    step_flop = gu_flop + 2 * P * spec.hidden * spec.inter
+
+    def step():
+        mq.expert_forward(layer, x_t, ids_t, rw_t, y=y, ws=ws)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(K):
+                step()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_per_step = wall_s * 1e3 / K
+    log(f"{K} steps: {ms_per_step * 1e3:.1f} us/layer")
+
+    # dominant kernel: the gate/up grouped GEMM (route and x quantisation done once)
+    xq, xs = mq.quantize_mxfp8(x_t)
+    mq.route(layer, ids_t, ws=ws)
+    hq = torch.empty((P, spec.inter), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((P, spec.inter // 32), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    graph_gu = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph_gu, stream=cap):
+            for _ in range(K):
+                mq.prefill_gate_up(layer, xq, xs, ids_t, hq=hq, hs=hs, ws=ws)
+        graph_gu.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(cap)
+        graph_gu.replay()
+        g1.record(cap)
+    torch.cuda.synchronize()
+    gu_us = g0.elapsed_time(g1) * 1e3 / K
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    gu_tflops = gu_flop / (gu_us * 1e-6) / 1e12
+    err = mq.check_device_error(ws)
+    if err:
+        sys.exit(f"device error word {err:#x}")
+    value = T / (ms_per_step * 1e-3)
+    out = {
+        "metric": "routed-MoE layer prefill tokens/s (T=2048, W4A8 grouped GEMM) + weight-stream GB/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8xfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": "DeepSeek-V4-Flash-shaped routed-MoE layer, prefill of 2048 tokens routed by a "
+                           "seeded hash of Zipf token ids: hidden 4096, 256 experts, intermediate 2048, "
+                           "top-6, MXFP4 weights x MXFP8 activations, fp32 accumulate",
+            "tokens_per_step": T,
+            "experts_touched": touched,
+            "expert_load_min_mean_max": [int(loads.min()), round(float(loads.mean()), 1), int(loads.max())],
+            "weight_bytes_per_step": step_bytes,
+            "flop_per_step": step_flop,
+            "launch": "HIP graph of the timed steps",
+            "parallelism": "single GPU",
+        },
+        "us_per_layer": round(ms_per_step * 1e3, 3),
+        "weight_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "layer_tflops": round(step_flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": {
+            "kernel": "prefill gate/up grouped GEMM (block-scaled FP8xFP4 MFMA) + SwiGLU + MXFP8 of h",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(wl.name),
+            "launch_us": round(gu_us, 3),
+            "algorithmic_bytes_per_launch": gu_bytes,
+            "mfma_tflops": round(gu_tflops, 2),
+            "mfma_peak_tflops": MFMA_FP8_PEAK_TFLOPS,
+            "mfma_frac": round(gu_tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+            "flop_per_launch": gu_flop,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline_prefill(wl, ids, rw, x_bits, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000 decode, 100 prefill)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mxfp4_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -137,6 +316,10 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "copies": 3}))
         return
     wl = workloads.WORKLOADS[args.workload]
+    if args.steps is None:
+        args.steps = 100 if wl.prefill else 2000
+    if wl.prefill:
+        return run_prefill(args, wl)
     spec = wl.spec
     K, W = args.steps, args.warmup
     log(f"workload {wl.name}: building layer ({spec.n_experts} experts) on the device")

@@ -105,11 +105,13 @@ bool prefill_path(const moeq_layer* L, int T) {
 
 struct WsLayout {
   size_t route, h, partial, xq, xs, hq, hs, total;
+  int P;
 };
 
 WsLayout ws_layout(const moeq_layer* L, int T) {
   const size_t P = (size_t)T * L->top_k;
   WsLayout w;
+  w.P = (int)P;
   size_t off = 256;  // header: device error word at 0
   w.route = off;
   off += align_up(RouteView::words(L->n_experts, (int)P) * 4, 256);
@@ -148,6 +150,7 @@ inline RouteView route_view(const moeq_layer* L, void* ws, const WsLayout& lay) 
   RouteView rv;
   rv.base = (int32_t*)((uint8_t*)ws + lay.route);
   rv.E = L->n_experts;
+  rv.P = lay.P;
   return rv;
 }
 
@@ -221,7 +224,8 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
 
 int check_prefill(const moeq_layer* L) {
   if (L->gate.fmt != MOEQ_FMT_MXFP4 || L->up.fmt != MOEQ_FMT_MXFP4 || L->down.fmt != MOEQ_FMT_MXFP4) return MOEQ_E_FMT;
-  if (L->hidden % 64 || L->inter % 64 || L->hidden % 128 || L->inter % 128) return MOEQ_E_SHAPE;
+  // K advances in chunks of 256 and a work-group covers 256 weight rows
+  if (L->hidden % 256 || L->inter % 256) return MOEQ_E_SHAPE;
   return MOEQ_OK;
 }
 
@@ -473,7 +477,7 @@ int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* 
   if (rc) return rc;
   if ((rc = check_prefill(L))) return rc;
   if (T < 0 || !xq || !xs || !ids || !hq || !hs) return MOEQ_E_INVAL;
-  if (!aligned(xq, 16) || (h_f32 && !aligned(h_f32, 4))) return MOEQ_E_ALIGN;
+  if (!aligned(xq, 16) || !aligned(xs, 8) || (h_f32 && !aligned(h_f32, 4))) return MOEQ_E_ALIGN;
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
   if (T == 0) return MOEQ_OK;
   return run_prefill_gate_up(L, xq, xs, T, h_f32, hq, hs, ws, ws_layout(L, T), S(stream));
@@ -485,7 +489,7 @@ int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs,
   if (rc) return rc;
   if ((rc = check_prefill(L))) return rc;
   if (T < 0 || !hq || !hs || !ids || !rw || !y) return MOEQ_E_INVAL;
-  if (!aligned(hq, 16) || !aligned(y, 4)) return MOEQ_E_ALIGN;
+  if (!aligned(hq, 16) || !aligned(hs, 8) || !aligned(y, 4)) return MOEQ_E_ALIGN;
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
   if (T == 0) return MOEQ_OK;
   if (T < 2) return MOEQ_E_SHAPE;  // the combine buffer exists for T > 1

@@ -53,6 +53,18 @@ __global__ __launch_bounds__(1024) void k_route(const int32_t* ids, int P, int E
   int f0 = (b0 < E && c0 > 0) ? 1 : 0, f1 = (b1 < E && c1 > 0) ? 1 : 0;
   int off = block_exclusive_scan(c0 + c1, tmp);
   int soff = block_exclusive_scan(f0 + f1, tmp);
+  // prefill work items: ceil(count / MC) per bucket, in bucket order
+  const int h0 = (c0 + PREFILL_MC - 1) / PREFILL_MC, h1 = (c1 + PREFILL_MC - 1) / PREFILL_MC;
+  const int hoff = block_exclusive_scan(h0 + h1, tmp);
+  for (int j = 0; j < h0; j++) {
+    rv.chunk_e()[hoff + j] = b0;
+    rv.chunk_m0()[hoff + j] = j * PREFILL_MC;
+  }
+  for (int j = 0; j < h1; j++) {
+    rv.chunk_e()[hoff + h0 + j] = b1;
+    rv.chunk_m0()[hoff + h0 + j] = j * PREFILL_MC;
+  }
+  if (t == (int)blockDim.x - 1) rv.n_chunks()[0] = hoff + h0 + h1;
   if (b0 <= E) {
     rv.offsets()[b0] = off;
     cur[b0] = off;

@@ -15,14 +15,25 @@ enum { EPI_SWIGLU = 0, EPI_PARTIAL = 1, EPI_PLAIN = 2 };
 //   [1, E + 2)         slot -> expert (E marks the bucket of out-of-range ids)
 //   [E + 2, 2E + 4)    bucket offsets into perm (bucket E = out-of-range ids)
 //   [2E + 4, ...)      perm: pair indices grouped by expert
+// Tokens per prefill work item (two 32-row tiles of the matrix instruction).
+constexpr int PREFILL_MC = 64;
+
 struct RouteView {
   int32_t* base;
-  int E;
+  int E, P;  // experts, (token, slot) pairs
   __host__ __device__ int32_t* n_slots() const { return base; }
   __host__ __device__ int32_t* slots() const { return base + 1; }
   __host__ __device__ int32_t* offsets() const { return base + E + 2; }
   __host__ __device__ int32_t* perm() const { return base + 2 * E + 4; }
-  static size_t words(int E, int P) { return (size_t)(2 * E + 4 + P); }
+  // Prefill work items: one per PREFILL_MC pairs of a bucket (bucket E holds the
+  // out-of-range ids), in bucket order: item q covers pairs chunk_m0[q] ..
+  // chunk_m0[q] + PREFILL_MC - 1 of bucket chunk_e[q].
+  __host__ __device__ int32_t* n_chunks() const { return base + 2 * E + 4 + P; }
+  __host__ __device__ int32_t* chunk_e() const { return base + 2 * E + 5 + P; }
+  __host__ __device__ int32_t* chunk_m0() const { return base + 2 * E + 5 + P + max_chunks(E, P); }
+  // sum over buckets of ceil(count / MC) <= P / MC + (non-empty buckets)
+  __host__ __device__ static int max_chunks(int E, int P) { return P / PREFILL_MC + (P < E + 1 ? P : E + 1); }
+  static size_t words(int E, int P) { return (size_t)(2 * E + 5 + P) + 2 * (size_t)max_chunks(E, P); }
 };
 
 struct WeightRef {

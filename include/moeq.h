@@ -164,8 +164,9 @@ int moeq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* y[T][H] (fp32, overwritten) of the routed layer for x[T][H] (bf16), expert ids
  * ids[T][K] (int32) and route weights rw[T][K] (fp32, applied after down as given).
- * Decode path (GEMV, any format) unless T >= 128 and gate, up and down are all
- * MXFP4, in which case the W4A8 prefill path runs (x and h quantised to MXFP8).
+ * Decode path (GEMV, any format) unless T >= 128, gate, up and down are all
+ * MXFP4 and hidden and inter are multiples of 256, in which case the W4A8 prefill
+ * path runs (x and h quantised to MXFP8).
  * T == 0 is a no-op. x, y 16-byte aligned. */
 int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y,
                         void* ws, size_t ws_bytes, void* stream);
@@ -186,11 +187,13 @@ int moeq_down(const moeq_layer* L, const float* h, const int32_t* ids, const flo
 int moeq_gate_up_timed(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws,
                        size_t ws_bytes, void* stream, void* start_event, void* stop_event);
 
-/* Stages of the W4A8 prefill path (MXFP4 weights only; moeq_route first).
- * moeq_prefill_gate_up: xq/xs = MXFP8 x (codes u8 [T][H], e8m0 u8 [T][H/32]) ->
- *   hq/hs = MXFP8 h (codes u8 [T*K][I], e8m0 u8 [T*K][I/32]); h_f32 (may be NULL)
- *   receives h before quantisation, fp32 [T*K][I].
- * moeq_prefill_down: hq/hs -> y[T][H]. */
+/* Stages of the W4A8 prefill path (MXFP4 weights only, hidden and inter multiples
+ * of 256; moeq_route first, on the same workspace).
+ * moeq_prefill_gate_up: xq/xs = MXFP8 x (codes u8 [T][H], 16-byte aligned; e8m0
+ *   u8 [T][H/32], 8-byte aligned) -> hq/hs = MXFP8 h (codes u8 [T*K][I], e8m0 u8
+ *   [T*K][I/32]); h_f32 (may be NULL) receives h before quantisation, fp32 [T*K][I].
+ * moeq_prefill_down: hq/hs (same alignment as xq/xs) -> y[T][H]; T >= 2.
+ * MOEQ_E_FMT for other formats, MOEQ_E_SHAPE for other shapes. */
 int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, const int32_t* ids, int T,
                          float* h_f32, uint8_t* hq, uint8_t* hs, void* ws, size_t ws_bytes, void* stream);
 int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, const int32_t* ids, const float* rw,

@@ -53,7 +53,7 @@ def pair_h(weight, xq, xs, t, e):
     # (H, I, E, K, T, seed)
     (512, 256, 8, 3, 40, 1),       # several experts with 1..30 tokens
     (1024, 512, 4, 2, 150, 2),     # > 64 tokens per expert: several passes of token tiles
-    (512, 384, 16, 6, 129, 3),     # T >= 128: expert_forward takes the prefill path
+    (512, 768, 16, 6, 129, 3),     # T >= 128: expert_forward takes the prefill path; 3 row groups
 ])
 def test_prefill_stages_small(case):
     H, I, E, K, T, seed = case
