@@ -224,13 +224,25 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
 
 int check_prefill(const moeq_layer* L) {
   if (L->gate.fmt != MOEQ_FMT_MXFP4 || L->up.fmt != MOEQ_FMT_MXFP4 || L->down.fmt != MOEQ_FMT_MXFP4) return MOEQ_E_FMT;
-  // K advances in chunks of 256 and a work-group covers 256 weight rows
+  // K advances in chunks of 256, a work-group covers 256 weight rows and holds
+  // the scales of all of K in LDS
   if (L->hidden % 256 || L->inter % 256) return MOEQ_E_SHAPE;
+  if (!prefill_fits(true, L->hidden) || !prefill_fits(false, L->inter)) return MOEQ_E_SHAPE;
+  // scales are staged in 8-byte pieces
+  for (const moeq_weight* w : {&L->gate, &L->up, &L->down})
+    if (!aligned(w->scales, 8) || w->scale_expert_stride % 8) return MOEQ_E_ALIGN;
   return MOEQ_OK;
+}
+
+// The prefill kernels address A (MXFP8 x, then MXFP8 h) with 32-bit offsets.
+bool prefill_a_fits(const moeq_layer* L, int T) {
+  const size_t lim = (size_t)1 << 31;
+  return (size_t)T * L->hidden < lim && (size_t)T * L->top_k * L->inter < lim;
 }
 
 int run_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, int T, float* h_f32,
                                uint8_t* hq, uint8_t* hs, void* ws, const WsLayout& lay, hipStream_t s) {
+  if (!prefill_a_fits(L, T)) return MOEQ_E_SHAPE;
   PrefillParams p;
   memset(&p, 0, sizeof(p));
   p.w[0] = ref_of(L->gate);
@@ -252,6 +264,7 @@ int run_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* x
 
 int run_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, const float* rw, int T, float* y,
                             void* ws, const WsLayout& lay, hipStream_t s) {
+  if (!prefill_a_fits(L, T)) return MOEQ_E_SHAPE;
   PrefillParams p;
   memset(&p, 0, sizeof(p));
   p.w[0] = ref_of(L->down);
@@ -437,7 +450,7 @@ int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, 
     rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_word(ws), s));
     if (rc) return rc;
   }
-  if (prefill_path(L, T) && check_prefill(L) == MOEQ_OK) {
+  if (prefill_path(L, T) && check_prefill(L) == MOEQ_OK && prefill_a_fits(L, T)) {
     uint8_t* xq = (uint8_t*)ws + lay.xq;
     uint8_t* xs = (uint8_t*)ws + lay.xs;
     uint8_t* hq = (uint8_t*)ws + lay.hq;

@@ -165,8 +165,8 @@ int moeq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 /* y[T][H] (fp32, overwritten) of the routed layer for x[T][H] (bf16), expert ids
  * ids[T][K] (int32) and route weights rw[T][K] (fp32, applied after down as given).
  * Decode path (GEMV, any format) unless T >= 128, gate, up and down are all
- * MXFP4 and hidden and inter are multiples of 256, in which case the W4A8 prefill
- * path runs (x and h quantised to MXFP8).
+ * MXFP4 and the layer meets the prefill stages' shape and alignment conditions
+ * (below), in which case the W4A8 prefill path runs (x and h quantised to MXFP8).
  * T == 0 is a no-op. x, y 16-byte aligned. */
 int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y,
                         void* ws, size_t ws_bytes, void* stream);
@@ -188,7 +188,10 @@ int moeq_gate_up_timed(const moeq_layer* L, const void* x, const int32_t* ids, i
                        size_t ws_bytes, void* stream, void* start_event, void* stop_event);
 
 /* Stages of the W4A8 prefill path (MXFP4 weights only, hidden and inter multiples
- * of 256; moeq_route first, on the same workspace).
+ * of 256, hidden at most 6400 and inter at most 12288 (a work-group holds the
+ * scales of its rows for all of K in LDS),
+ * weight scale planes and their expert stride 8-byte aligned (else MOEQ_E_ALIGN);
+ * moeq_route first, on the same workspace).
  * moeq_prefill_gate_up: xq/xs = MXFP8 x (codes u8 [T][H], 16-byte aligned; e8m0
  *   u8 [T][H/32], 8-byte aligned) -> hq/hs = MXFP8 h (codes u8 [T*K][I], e8m0 u8
  *   [T*K][I/32]); h_f32 (may be NULL) receives h before quantisation, fp32 [T*K][I].
