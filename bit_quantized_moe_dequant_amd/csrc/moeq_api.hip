@@ -224,10 +224,8 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
 
 int check_prefill(const moeq_layer* L) {
   if (L->gate.fmt != MOEQ_FMT_MXFP4 || L->up.fmt != MOEQ_FMT_MXFP4 || L->down.fmt != MOEQ_FMT_MXFP4) return MOEQ_E_FMT;
-  // K advances in chunks of 256, a work-group covers 256 weight rows and holds
-  // the scales of all of K in LDS
+  // K advances in chunks of 256 and a work-group covers 256 weight rows
   if (L->hidden % 256 || L->inter % 256) return MOEQ_E_SHAPE;
-  if (!prefill_fits(true, L->hidden) || !prefill_fits(false, L->inter)) return MOEQ_E_SHAPE;
   // scales are staged in 8-byte pieces
   for (const moeq_weight* w : {&L->gate, &L->up, &L->down})
     if (!aligned(w->scales, 8) || w->scale_expert_stride % 8) return MOEQ_E_ALIGN;
@@ -429,7 +427,7 @@ int moeq_down(const moeq_layer* L, const float* h, const int32_t* ids, const flo
   int rc = check_layer(L);
   if (rc) return rc;
   if (T < 0 || !h || !ids || !rw || !y) return MOEQ_E_INVAL;
-  if (!aligned(h, 16) || !aligned(y, 4)) return MOEQ_E_ALIGN;
+  if (!aligned(h, 16) || !aligned(y, 16)) return MOEQ_E_ALIGN;
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
   if (T == 0) return MOEQ_OK;
   return run_down(L, h, ids, rw, T, y, ws, ws_layout(L, T), S(stream));
@@ -502,7 +500,7 @@ int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs,
   if (rc) return rc;
   if ((rc = check_prefill(L))) return rc;
   if (T < 0 || !hq || !hs || !ids || !rw || !y) return MOEQ_E_INVAL;
-  if (!aligned(hq, 16) || !aligned(hs, 8) || !aligned(y, 4)) return MOEQ_E_ALIGN;
+  if (!aligned(hq, 16) || !aligned(hs, 8) || !aligned(y, 16)) return MOEQ_E_ALIGN;
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
   if (T == 0) return MOEQ_OK;
   if (T < 2) return MOEQ_E_SHAPE;  // the combine buffer exists for T > 1

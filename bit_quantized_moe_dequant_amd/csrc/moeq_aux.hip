@@ -99,19 +99,26 @@ hipError_t launch_route(const int32_t* ids, int P, int E, RouteView rv, uint32_t
 }
 
 // ---------------------------------------------------------------- combine
-// y[t][r] = sum over k in slot order of partial[t*K + k][r].
+// y[t][r] = sum over k in slot order of partial[t*K + k][r]; four outputs per
+// thread (H is a multiple of 4: every format's K-block is).
 __global__ __launch_bounds__(256) void k_combine(const float* partial, int T, int K, int H, float* y) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= (size_t)T * H) return;
-  size_t t = i / H, r = i % H;
+  const size_t t = i / H, r = i % H;
   const float* p = partial + t * K * (size_t)H + r;
-  float acc = 0.f;
-  for (int k = 0; k < K; k++) acc += p[(size_t)k * H];
-  y[i] = acc;
+  float4 acc = *reinterpret_cast<const float4*>(p);
+  for (int k = 1; k < K; k++) {
+    const float4 v = *reinterpret_cast<const float4*>(p + (size_t)k * H);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(y + i) = acc;
 }
 
 hipError_t launch_combine(const float* partial, int T, int K, int H, float* y, hipStream_t s) {
-  size_t n = (size_t)T * H;
+  const size_t n = (size_t)T * H / 4;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, partial, T, K, H, y);
   return hipGetLastError();
 }

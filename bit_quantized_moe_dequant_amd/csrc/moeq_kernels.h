@@ -122,8 +122,6 @@ hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s);
 bool fused1_supported(int fg, int fd, int hidden, int inter, int top_k);
 hipError_t launch_fused1(int fg, int fd, const FusedParams& p, hipStream_t s);
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int n_slots, hipStream_t s);
-// whether a prefill pass with this K (cols) fits its staged scales in LDS
-bool prefill_fits(bool gate_up, int cols);
 
 // Chunk geometry: weights per 16-byte chunk; lanes per row and chunks per lane.
 int weights_per_chunk(int fmt);

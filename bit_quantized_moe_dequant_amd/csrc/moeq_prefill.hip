@@ -26,11 +26,12 @@
 // rows: for gate/up it streams the gate and the up rows of the same 32 features,
 // which share every A fragment it reads (half the LDS reads per matrix
 // instruction, and SwiGLU needs no exchange); for down one 32-row tile, which
-// leaves registers for two work-groups per compute unit. K advances in chunks of 256 (eight 32-blocks): the
-// chunk's A tile (64 token rows x 256 bytes, gathered through the routing
-// permutation) is staged once in LDS, double-buffered, and shared by the eight
-// waves; the weights go straight from HBM to registers one chunk ahead. Items
-// with at most 32 pairs skip the second token tile's instructions.
+// leaves registers for two work-groups per compute unit. K advances in chunks of
+// 256 (eight 32-blocks): the chunk's A tile (64 token rows x 256 bytes, gathered
+// through the routing permutation) is staged once in LDS, double-buffered, and
+// shared by the eight waves; the weights go straight from HBM to registers one
+// chunk ahead. Items with at most 32 pairs skip the second token tile's
+// instructions.
 //
 // Order of K inside a chunk. The contraction is a sum, so any order of the eight
 // 32-blocks is the same product as long as A, B and both scales follow it. The
@@ -41,7 +42,7 @@
 #include "moeq_device.h"
 #include "moeq_kernels.h"
 
-#include <mutex>
+#include <type_traits>
 
 namespace moeq {
 
@@ -100,20 +101,26 @@ __device__ __forceinline__ int byte_of(uint32_t w, int i) { return (int)((w >> (
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Raw buffer of a uniform base: loads take a 32-bit per-lane offset and a uniform
+// offset (the address stays in scalar registers; no 64-bit per-lane pointers).
+// 0x00020000 is the gfx9-family buffer descriptor format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
 // One chunk of a wave's weight tile: lane (n, g) holds bytes [64g, 64g + 64) of
 // row n's 128-byte chunk.
 struct BChunk {
   i32x4 q[4];
 };
 
-// Dynamic LDS of a work-group: the item's scales for all of K, staged once (rows
-// padded by 16 bytes: a 32-lane read of one column then touches two rows per
-// bank at most). A: [64 token rows][SP]; B: [NS][256 rows][SP], SP = cols/32 + 16.
-__host__ __device__ constexpr int pf_scale_stride(int cols) { return cols / 32 + 16; }
+// Scales are staged in groups of PF_SG chunks (8 bytes per row per chunk) in a
+// two-slot LDS ring, loaded PF_SG stages ahead of use, so every scale line of
+// HBM is requested once per group instead of once per chunk. Rows are padded to
+// 36 bytes (nine words), so a 32-lane read of one word column is conflict-free.
+constexpr int PF_SG = 4;
+constexpr int PF_SROW = 8 * PF_SG + 4;
 __host__ __device__ constexpr int pf_weight_tiles(bool gate_up) { return gate_up ? 2 : 1; }
-size_t pf_dynamic_lds(bool gate_up, int cols) {
-  return (size_t)(PREFILL_MC + pf_weight_tiles(gate_up) * pf_rows(gate_up)) * pf_scale_stride(cols);
-}
 
 // down: 16 waves per compute unit (two work-groups), gate/up: what fits
 template <bool GATE_UP>
@@ -123,9 +130,11 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
   // down one
   constexpr int NS = pf_weight_tiles(GATE_UP);
   constexpr int ROWS = pf_rows(GATE_UP);
+  constexpr int NBP = NS * ROWS * PF_SG / PF_THREADS;  // weight-scale pieces per thread per group
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][PREFILL_MC][PF_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t bs_ring[2][NS * ROWS][PF_SROW];
+  __shared__ __attribute__((aligned(16))) uint8_t as_ring[2][PREFILL_MC][PF_SROW];
   __shared__ int pair_lds[PREFILL_MC];
-  extern __shared__ __attribute__((aligned(16))) uint8_t pf_dyn[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -156,24 +165,23 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
 
   const int n = lane & 31, g = lane >> 5;
   const int nchunks = P.cols / PF_KC;
-  const int ncw = P.cols / 128;  // 32-bit words of scales per row
-  const int SP = pf_scale_stride(P.cols);
   const bool two_tiles = M > 32;
   const int n0 = nbase + wave * 32;  // this wave's 32 weight rows (gate/up: of both matrices)
-  uint8_t* as_all = pf_dyn;
-  uint8_t* bs_all = pf_dyn + PREFILL_MC * SP;
-  const uint8_t* b_base[NS];
+  __amdgpu_buffer_rsrc_t b_buf[NS], bs_buf[NS];
 #pragma unroll
-  for (int s = 0; s < NS; s++) b_base[s] = P.w[s].data + (size_t)e * P.w[s].estride;
+  for (int s = 0; s < NS; s++) {
+    b_buf[s] = raw_buffer(P.w[s].data + (size_t)e * P.w[s].estride);
+    bs_buf[s] = raw_buffer(P.w[s].scales + (size_t)e * P.w[s].sestride);
+  }
+  const __amdgpu_buffer_rsrc_t a_buf = raw_buffer(P.aq), as_buf = raw_buffer(P.as);
   const uint32_t b_off = (uint32_t)(n0 + n) * (uint32_t)(P.cols / 2) + 64u * g;
 
   // Every load of the K loop is unconditional (token rows past M read pair 0's
   // row, chunks past the end re-read the last one): loads complete in issue order
   // and the compiler can then wait for exactly the oldest ones instead of draining
-  // the queue. A pieces are 32-bit offsets from the uniform base (A has fewer
+  // the queue. Per-lane parts are 32-bit offsets from uniform bases (A has fewer
   // than 2^31 bytes, checked by the caller).
   uint32_t a_off[PF_PIECES];
-  int a_dst[PF_PIECES];
 #pragma unroll
   for (int j = 0; j < PF_PIECES; j++) {
     const int piece = tid + PF_THREADS * j;  // 0..1023
@@ -181,14 +189,32 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
     const int pr = pair_lds[r < M ? r : 0];
     const uint32_t arow = (uint32_t)(GATE_UP ? pr / P.top_k : pr);
     a_off[j] = arow * (uint32_t)P.cols + 16u * c16;
-    a_dst[j] = r * PF_STRIDE + 16 * c16;
+  }
+  // LDS place of A piece j (recomputed at each use: cheaper than a register)
+  auto a_dst = [&](int j) {
+    const int piece = tid + PF_THREADS * j;
+    return (piece >> 4) * PF_STRIDE + 16 * (piece & 15);
+  };
+  // Scale pieces of this thread: weight piece j is (tile, row, chunk k of the
+  // group) of i = tid + PF_THREADS j with k = i % PF_SG, row = (i / PF_SG) % ROWS and
+  // tile = i / (PF_SG ROWS) = PF_THREADS j / (PF_SG ROWS), known per j; the A piece
+  // is (token row, k) of tid mod 256 (threads 256 apart load and store the same piece).
+  static_assert((PF_SG * ROWS) % PF_THREADS == 0, "a weight-scale piece's tile is fixed per j");
+  const int sk = tid % PF_SG;
+  uint32_t as_src;
+  {
+    const int r = (tid & 255) / PF_SG;
+    const int pr = pair_lds[r < M ? r : 0];
+    const uint32_t arow = (uint32_t)(GATE_UP ? pr / P.top_k : pr);
+    as_src = arow * (uint32_t)(P.cols / 32);
   }
 
   u32x4 a_pre[PF_PIECES];
+  uint2 bs_pre[NBP], as_pre;
   auto load_a = [&](int c) {
     c = min(c, nchunks - 1);
 #pragma unroll
-    for (int j = 0; j < PF_PIECES; j++) a_pre[j] = ld16(P.aq + a_off[j] + c * PF_KC);
+    for (int j = 0; j < PF_PIECES; j++) a_pre[j] = __builtin_amdgcn_raw_buffer_load_b128(a_buf, a_off[j], c * PF_KC, 0);
   };
   auto load_b = [&](int c, BChunk (&b)[NS]) {
     c = min(c, nchunks - 1);
@@ -196,7 +222,39 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
     for (int s = 0; s < NS; s++)
 #pragma unroll
       for (int i = 0; i < 4; i++)
-        b[s].q[i] = *reinterpret_cast<const i32x4*>(b_base[s] + b_off + c * (PF_KC / 2) + 16 * i);
+        b[s].q[i] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_raw_buffer_load_b128(b_buf[s], b_off + 16 * i, c * (PF_KC / 2), 0));
+  };
+  // scales of group G (chunks PF_SG G ..): the chunk index is clamped per piece
+  auto load_scales = [&](int G) {
+    // chunk PF_SG G + min(sk, last - PF_SG G): uniform part in the scalar offset
+    const int kk = 8 * min(sk, nchunks - 1 - PF_SG * G);
+#pragma unroll
+    for (int j = 0; j < NBP; j++) {
+      const int i = tid + PF_THREADS * j;
+      const int s = (PF_THREADS * j) / (PF_SG * ROWS);
+      const int row = (i / PF_SG) % ROWS;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+          bs_buf[s], (uint32_t)(nbase + row) * (uint32_t)(P.cols / 32) + kk, 8 * PF_SG * G, 0);
+      bs_pre[j] = make_uint2(v[0], v[1]);
+    }
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(as_buf, as_src + kk, 8 * PF_SG * G, 0);
+    as_pre = make_uint2(v[0], v[1]);
+  };
+  auto store_scales = [&](int G) {
+    const int slot = G & 1;
+#pragma unroll
+    for (int j = 0; j < NBP; j++) {
+      const int i = tid + PF_THREADS * j;
+      const int s = (PF_THREADS * j) / (PF_SG * ROWS);
+      const int row = (i / PF_SG) % ROWS;
+      uint32_t* d = reinterpret_cast<uint32_t*>(&bs_ring[slot][s * ROWS + row][8 * sk]);
+      d[0] = bs_pre[j].x;
+      d[1] = bs_pre[j].y;
+    }
+    uint32_t* d = reinterpret_cast<uint32_t*>(&as_ring[slot][(tid & 255) / PF_SG][8 * sk]);
+    d[0] = as_pre.x;  // threads 256 apart store the same piece, same value
+    d[1] = as_pre.y;
   };
   // A fragment of K step i for token tile t from LDS buffer buf.
   auto read_a = [&](int buf, int i, int t) {
@@ -206,60 +264,13 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
     return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // the four scales of chunk c for this lane: token tile t (A), weight tile s (B)
-  auto a_scales = [&](int c, int t) { return *reinterpret_cast<const uint32_t*>(as_all + (32 * t + n) * SP + 8 * c + 4 * g); };
+  auto a_scales = [&](int c, int t) {
+    return *reinterpret_cast<const uint32_t*>(&as_ring[(c / PF_SG) & 1][32 * t + n][8 * (c % PF_SG) + 4 * g]);
+  };
   auto b_scales = [&](int c, int s) {
-    return *reinterpret_cast<const uint32_t*>(bs_all + (s * ROWS + wave * 32 + n) * SP + 8 * c + 4 * g);
+    return *reinterpret_cast<const uint32_t*>(
+        &bs_ring[(c / PF_SG) & 1][s * ROWS + wave * 32 + n][8 * (c % PF_SG) + 4 * g]);
   };
-
-  // Stage the scales of all of K, 8-byte pieces: the work-group's weight rows
-  // (contiguous in the scale plane) and the item's token rows (gathered; rows
-  // past M take pair 0's row, their results are never stored). The loads of a
-  // batch are all issued, then the pipeline's first A and B loads, then the LDS
-  // stores; the first stage's barrier publishes them.
-  constexpr int SB = 32;  // pieces per thread per batch (one batch up to K = 4096)
-  const int npr = P.cols / 256;  // 8-byte pieces per row
-  const int nbp = NS * ROWS * npr, nap = PREFILL_MC * npr;
-  auto scale_piece = [&](int i, const uint8_t*& src, uint8_t*& dst) {
-    if (i < nbp) {
-      const int s = i / (ROWS * npr), rem = i % (ROWS * npr), row = rem / npr, w8 = rem % npr;
-      src = P.w[s].scales + (size_t)e * P.w[s].sestride + (size_t)(nbase + row) * (P.cols / 32) + 8 * w8;
-      dst = bs_all + (s * ROWS + row) * SP + 8 * w8;
-    } else {
-      const int j = i - nbp, r = j / npr, w8 = j % npr;
-      const int pr = pair_lds[r < M ? r : 0];
-      const size_t arow = (size_t)(GATE_UP ? pr / P.top_k : pr);
-      src = P.as + arow * (P.cols / 32) + 8 * w8;
-      dst = as_all + r * SP + 8 * w8;
-    }
-  };
-  bool started = false;
-  for (int base = 0; base < nbp + nap; base += SB * PF_THREADS) {
-    uint2 v[SB];
-#pragma unroll
-    for (int j = 0; j < SB; j++) {
-      const int i = base + j * PF_THREADS + tid;
-      if (i < nbp + nap) {
-        const uint8_t* src;
-        uint8_t* dst;
-        scale_piece(i, src, dst);
-        v[j] = *reinterpret_cast<const uint2*>(src);
-      }
-    }
-    if (!started) {
-      load_a(0);
-      started = true;
-    }
-#pragma unroll
-    for (int j = 0; j < SB; j++) {
-      const int i = base + j * PF_THREADS + tid;
-      if (i < nbp + nap) {
-        const uint8_t* src;
-        uint8_t* dst;
-        scale_piece(i, src, dst);
-        *reinterpret_cast<uint2*>(dst) = v[j];
-      }
-    }
-  }
 
   v16f acc[NS][2];  // [weight tile][token tile]
 #pragma unroll
@@ -269,16 +280,22 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[s][t][r] = 0.f;
 
-  // One chunk: publish A(c) in LDS, prefetch A(c + 1) then B(c + 1) (in that
-  // order, so waiting for A never waits for the newer B), then the four K steps
-  // on B(c). A stage past the last chunk only keeps the pipeline's shape.
-  auto stage = [&](int c, const BChunk (&cur)[NS], BChunk (&pre)[NS]) {
+  // One chunk: publish A(c) (and, two stages into a group, the next group's
+  // scales) in LDS, prefetch A(c + 1) then B(c + 1) (in that order, so waiting for
+  // A never waits for the newer B; at a group's first stage the next group's
+  // scales follow), then the four K steps on B(c). A stage past the last chunk
+  // only keeps the pipeline's shape. SC: 1 = issue the next group's scale loads,
+  // 2 = store them.
+  auto stage = [&](auto sc_tag, int c, const BChunk (&cur)[NS], BChunk (&pre)[NS]) {
+    constexpr int SC = decltype(sc_tag)::value;
     const int buf = c & 1;
 #pragma unroll
-    for (int j = 0; j < PF_PIECES; j++) *reinterpret_cast<u32x4*>(&a_lds[buf][0][0] + a_dst[j]) = a_pre[j];
+    for (int j = 0; j < PF_PIECES; j++) *reinterpret_cast<u32x4*>(&a_lds[buf][0][0] + a_dst(j)) = a_pre[j];
+    if constexpr (SC == 2) store_scales(c / PF_SG + 1);
     __syncthreads();
     load_a(c + 1);
     load_b(c + 1, pre);
+    if constexpr (SC == 1) load_scales(c / PF_SG + 1);
     // keep the next stage's LDS stores (which wait for A(c + 1)) out of this
     // stage's matrix instructions
     __builtin_amdgcn_sched_barrier(0);
@@ -292,14 +309,16 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
       // work-groups per compute unit)
       if (two_tiles) {
         const uint32_t sa1 = a_scales(c, 1);
+        // token tiles one after the other: one fragment live at a time
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          // an e2m1 operand occupies the low four registers of the tuple; the
-          // instruction does not read the upper four
-          const v8i b = __builtin_shufflevector(cur[0].q[i], cur[0].q[i], 0, 1, 2, 3, -1, -1, -1, -1);
-          acc[0][0] = mfma_fp8_fp4(read_a(buf, i, 0), b, acc[0][0], byte_of(sa0, i), byte_of(sb[0], i));
-          acc[0][1] = mfma_fp8_fp4(read_a(buf, i, 1), b, acc[0][1], byte_of(sa1, i), byte_of(sb[0], i));
-        }
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            // an e2m1 operand occupies the low four registers of the tuple; the
+            // instruction does not read the upper four
+            const v8i b = __builtin_shufflevector(cur[0].q[i], cur[0].q[i], 0, 1, 2, 3, -1, -1, -1, -1);
+            acc[0][t] = mfma_fp8_fp4(read_a(buf, i, t), b, acc[0][t], byte_of(t ? sa1 : sa0, i), byte_of(sb[0], i));
+          }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -361,12 +380,23 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  __builtin_amdgcn_sched_barrier(0);  // A(0) (issued with the scales) before B(0)
+  // prologue: group 0's scales, A(0), B(0); then group 0's scales into LDS (the
+  // first stage's barrier publishes them)
+  load_scales(0);
+  load_a(0);
+  __builtin_amdgcn_sched_barrier(0);  // A(0) before B(0), as every stage issues A before B
   BChunk b0[NS], b1[NS];
   load_b(0, b0);
-  for (int c = 0; c < nchunks; c += 2) {
-    stage(c, b0, b1);
-    stage(c + 1, b1, b0);
+  store_scales(0);
+  using none = std::integral_constant<int, 0>;
+  using issue = std::integral_constant<int, 1>;
+  using store = std::integral_constant<int, 2>;
+  static_assert(PF_SG == 4, "the loop body below is one group of four stages");
+  for (int c = 0; c < nchunks; c += PF_SG) {
+    stage(issue{}, c, b0, b1);
+    stage(none{}, c + 1, b1, b0);
+    stage(store{}, c + 2, b0, b1);
+    stage(none{}, c + 3, b1, b0);
   }
 
   // epilogue
@@ -399,26 +429,11 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
   }
 }
 
-bool prefill_fits(bool gate_up, int cols) {
-  return pf_dynamic_lds(gate_up, cols) + 2 * PREFILL_MC * PF_STRIDE + 4 * PREFILL_MC <= 160 * 1024;
-}
-
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int /*n_slots*/, hipStream_t s) {
-  // rows and cols are multiples of 256 and the scales fit in LDS (checked by the caller)
-  static std::once_flag lds_once;
-  static hipError_t lds_rc = hipSuccess;
-  std::call_once(lds_once, [] {
-    // allow the largest dynamic LDS the checks admit
-    const int dyn = 160 * 1024 - (int)(2 * PREFILL_MC * PF_STRIDE + 4 * PREFILL_MC);
-    lds_rc = hipFuncSetAttribute((const void*)k_prefill<true>, hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
-    if (lds_rc == hipSuccess)
-      lds_rc = hipFuncSetAttribute((const void*)k_prefill<false>, hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
-  });
-  if (lds_rc != hipSuccess) return lds_rc;
-  const size_t dyn = pf_dynamic_lds(gate_up, p.cols);
+  // rows and cols are multiples of 256 (checked by the caller)
   dim3 g((unsigned)(p.rows / pf_rows(gate_up)), (unsigned)RouteView::max_chunks(p.route.E, p.route.P)), b(PF_THREADS);
-  if (gate_up) hipLaunchKernelGGL(k_prefill<true>, g, b, dyn, s, p);
-  else hipLaunchKernelGGL(k_prefill<false>, g, b, dyn, s, p);
+  if (gate_up) hipLaunchKernelGGL(k_prefill<true>, g, b, 0, s, p);
+  else hipLaunchKernelGGL(k_prefill<false>, g, b, 0, s, p);
   return hipGetLastError();
 }
 

@@ -174,7 +174,8 @@ int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, 
 /* Stages of the decode path, for tests and timing (moeq_expert_forward runs them
  * in order). moeq_route groups the T*K (token, slot) pairs by expert into the
  * workspace (needed before the other two when T > 1). moeq_gate_up writes
- * h[T][K][I] (fp32) = silu(G x) * (U x) per pair. moeq_down writes y[T][H]. */
+ * h[T][K][I] (fp32) = silu(G x) * (U x) per pair. moeq_down writes y[T][H].
+ * x, h, y 16-byte aligned. */
 int moeq_route(const moeq_layer* L, const int32_t* ids, int T, void* ws, size_t ws_bytes, void* stream);
 int moeq_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, size_t ws_bytes,
                  void* stream);
@@ -188,14 +189,14 @@ int moeq_gate_up_timed(const moeq_layer* L, const void* x, const int32_t* ids, i
                        size_t ws_bytes, void* stream, void* start_event, void* stop_event);
 
 /* Stages of the W4A8 prefill path (MXFP4 weights only, hidden and inter multiples
- * of 256, hidden at most 6400 and inter at most 12288 (a work-group holds the
- * scales of its rows for all of K in LDS),
- * weight scale planes and their expert stride 8-byte aligned (else MOEQ_E_ALIGN);
+ * of 256, weight scale planes and their expert stride 8-byte aligned, else
+ * MOEQ_E_ALIGN);
  * moeq_route first, on the same workspace).
  * moeq_prefill_gate_up: xq/xs = MXFP8 x (codes u8 [T][H], 16-byte aligned; e8m0
  *   u8 [T][H/32], 8-byte aligned) -> hq/hs = MXFP8 h (codes u8 [T*K][I], e8m0 u8
  *   [T*K][I/32]); h_f32 (may be NULL) receives h before quantisation, fp32 [T*K][I].
- * moeq_prefill_down: hq/hs (same alignment as xq/xs) -> y[T][H]; T >= 2.
+ * moeq_prefill_down: hq/hs (same alignment as xq/xs) -> y[T][H] (16-byte
+ *   aligned); T >= 2.
  * MOEQ_E_FMT for other formats, MOEQ_E_SHAPE for other shapes. */
 int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, const int32_t* ids, int T,
                          float* h_f32, uint8_t* hq, uint8_t* hs, void* ws, size_t ws_bytes, void* stream);
