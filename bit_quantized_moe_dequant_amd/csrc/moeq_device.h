@@ -149,8 +149,7 @@ struct WView {
 };
 
 struct Iq2Lds {
-  uint32_t grid[256 * 4];
-  uint32_t sign[128 * 4];
+  uint32_t grid[256 * 4];  // codebook entry i as four bf16 pairs (values 0..255: sign bits clear)
 };
 
 template <int FMT> struct Dec;
@@ -384,11 +383,18 @@ __device__ __forceinline__ void iq2_fill_lds(Iq2Lds* t, const uint8_t* grid, int
     uint32_t g0 = grid[2 * i], g1 = grid[2 * i + 1];
     t->grid[i] = (f32_bf16_rne((float)g0)) | (f32_bf16_rne((float)g1) << 16);
   }
-  for (int i = tid; i < 128 * 4; i += nthreads) {
-    uint32_t c = (uint32_t)(i >> 2), k = (uint32_t)(i & 3);
-    uint32_t m = c | ((uint32_t)(__builtin_popcount(c) & 1) << 7);
-    t->sign[i] = (((m >> (2 * k)) & 1u) << 15) | (((m >> (2 * k + 1)) & 1u) << 31);
-  }
+}
+
+// The four bf16-pair sign masks of one IQ2_XXS group from its 7-bit sign code c:
+// the 8-bit mask m is c plus its parity bit (an even number of negatives); word k
+// carries m bit 2k at bit 15 and m bit 2k + 1 at bit 31. With Y = m << 15 | m << 30
+// as a 64-bit value (two copies that do not overlap), word k is bits [2k, 2k + 32)
+// of Y, masked to 0x80008000.
+__device__ __forceinline__ void iq2_sign_words(uint32_t c, uint32_t* w) {
+  const uint32_t m = c | ((uint32_t)(__builtin_popcount(c) & 1) << 7);
+  const uint32_t ylo = (m << 15) | (m << 30), yhi = m >> 2;
+#pragma unroll
+  for (int k = 0; k < 4; k++) w[k] = __builtin_amdgcn_alignbit(yhi, ylo, 2 * k) & 0x80008000u;
 }
 template <> struct Dec<FMT_IQ2_XXS> {
   static constexpr int WPC = 64;
@@ -415,9 +421,11 @@ template <> struct Dec<FMT_IQ2_XXS> {
         uint32_t gi = (a0 >> (8 * l)) & 0xFFu;
         uint32_t c = (a1 >> (7 * l)) & 0x7Fu;
         u32x4 g = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
-        u32x4 m = *reinterpret_cast<const u32x4*>(&t->sign[c * 4]);
+        uint32_t m[4];
+        iq2_sign_words(c, m);  // in registers: an LDS lookup per group costs more here
+        // sign bits of the codebook words are clear, so OR applies the signs
 #pragma unroll
-        for (int k = 0; k < 4; k++) S = dotp<ACT, 64>(g[k] ^ m[k], x, 16 * j + 4 * l + k, S);
+        for (int k = 0; k < 4; k++) S = dotp<ACT, 64>(g[k] | m[k], x, 16 * j + 4 * l + k, S);
       }
       float db = d8 * (float)(2u * (a1 >> 28) + 1u);
       acc = __builtin_fmaf(db, S, acc);
