@@ -54,6 +54,7 @@ def pair_h(weight, xq, xs, t, e):
     (512, 256, 8, 3, 40, 1),       # several experts with 1..30 tokens
     (1024, 512, 4, 2, 150, 2),     # > 64 tokens per expert: several passes of token tiles
     (512, 768, 16, 6, 129, 3),     # T >= 128: expert_forward takes the prefill path; 3 row groups
+    (1280, 512, 8, 2, 200, 4),     # K = 1280: five 256-chunks, a partial second group of staged scales
 ])
 def test_prefill_stages_small(case):
     H, I, E, K, T, seed = case
@@ -142,3 +143,32 @@ def test_prefill_full_size_sampled():
     assert np.array_equal(out["y_fwd"], out["y"])
     del layer
     torch.cuda.empty_cache()
+
+
+def test_prefill_item_boundaries():
+    """Expert loads chosen at the work-item edges: 1, 32 (one token tile), 33 (a
+    second tile), 64 (one full item), 65 (a second item of one pair) and 128 (two
+    full items); the other pairs go to the remaining experts."""
+    say("prefill item boundaries")
+    H, I, E, K, T = 512, 256, 8, 2, 200
+    spec = workloads.LayerSpec(H, I, E, K, mq.FMT_MXFP4, mq.FMT_MXFP4, seed=4200)
+    layer = upload_layer(spec)
+    loads = [1, 32, 33, 64, 65, 128]
+    flat = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(loads)])
+    rest = T * K - flat.size
+    flat = np.concatenate([flat, 6 + (np.arange(rest) % 2).astype(np.int32)])
+    rng = np.random.default_rng(4201)
+    ids = rng.permutation(flat).reshape(T, K).astype(np.int32)   # duplicates within a token allowed
+    _, rw = synth.uniform_routing(4202, T, E, K)
+    x = synth.activations_bf16(4203, T, H)
+    assert list(np.bincount(ids.reshape(-1), minlength=E)[:6]) == loads
+    out = run_stages(layer, x, ids, rw)
+    assert out["err"] == 0
+    weight = oracle_weight_fn(spec)
+    ref_h = moe.prefill_h(out["xq"], out["xs"], ids, weight).reshape(T * K, I)
+    assert rel_err(out["h"], ref_h) < TOL
+    q2, s2 = mxfp8.quantize(out["h"].astype(np.float64))
+    assert np.array_equal(out["hq"], q2) and np.array_equal(out["hs"], s2)
+    ref_y = moe.prefill_y(out["hq"], out["hs"], ids, rw, weight)
+    assert rel_err(out["y"], ref_y) < TOL
+    assert np.array_equal(out["y_fwd"], out["y"])
