@@ -7,6 +7,8 @@
 #include "moeq.h"
 #include "moeq_kernels.h"
 
+#include <cmath>
+
 using namespace moeq;
 
 namespace {
@@ -172,6 +174,20 @@ GemvParams gemv_params(const moeq_layer* L, const moeq_weight& a, const moeq_wei
   return p;
 }
 
+// Token tile of the grouped GEMVs (T > 1): the pairs of an expert are processed
+// this many at a time. The tile's register cost (activations of every token it
+// holds) lowers occupancy, and at a few tokens per expert most of it would be
+// padding, so the width follows the expected pairs per touched expert under
+// uniform routing, P / (E (1 - (1 - K/E)^T)). #ifndef lets a build pin it.
+#ifndef MOEQ_GROUPED_WIDE_FROM
+#define MOEQ_GROUPED_WIDE_FROM 2.5
+#endif
+bool grouped_wide(const moeq_layer* L, int T) {
+  const double E = L->n_experts, K = L->top_k;
+  const double touched = E * (1.0 - std::pow(1.0 - K / E, (double)T));
+  return (double)T * K / (touched > 1.0 ? touched : 1.0) >= MOEQ_GROUPED_WIDE_FROM;
+}
+
 int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
                 hipStream_t s, const LaunchEvents* ev = nullptr) {
   GemvParams p = gemv_params(L, L->gate, &L->up, ws, lay);
@@ -186,7 +202,7 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
   p.mode = MODE_GROUPED;
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
-  return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, 4, s, ev));
+  return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, grouped_wide(L, T) ? 4 : 1, s, ev));
 }
 
 int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
@@ -217,7 +233,7 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
   p.out = partial;
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
-  int rc = hip_rc(launch_gemv(L->down.fmt, EPI_PARTIAL, p, slots, 2, s));
+  int rc = hip_rc(launch_gemv(L->down.fmt, EPI_PARTIAL, p, slots, grouped_wide(L, T) ? 2 : 1, s));
   if (rc) return rc;
   return hip_rc(launch_combine(partial, T, L->top_k, L->hidden, y, s));
 }

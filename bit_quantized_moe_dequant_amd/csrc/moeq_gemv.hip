@@ -391,7 +391,8 @@ static hipError_t gemv_fc(int epi, const GemvParams& p, dim3 g, int mt, hipStrea
     if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
     else MOEQ_LAUNCH((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
   } else if (epi == EPI_PARTIAL) {
-    MOEQ_LAUNCH((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
+    if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
+    else MOEQ_LAUNCH((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
   } else {
     if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
     else MOEQ_LAUNCH((k_gemv<FMT, CPL, 4, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
