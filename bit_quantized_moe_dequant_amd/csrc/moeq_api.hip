@@ -524,12 +524,26 @@ int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs,
 }
 
 int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y, void* stream) {
-  int rc = check_weight(w, true);
+  int rc = check_weight(w, false);
   if (rc) return rc;
+  const bool mfma = w->fmt == MOEQ_FMT_FP8_B128 && T > 1 && linear_fp8_fits(w->rows, w->cols);
+  int lpr, cpl;
+  if (!mfma && !chunk_geometry(w->fmt, w->cols, &lpr, &cpl)) return MOEQ_E_SHAPE;
   if (expert < 0 || expert >= w->n_experts || T < 0 || !x || !y) return MOEQ_E_INVAL;
   if (!aligned(x, 16) || !aligned(y, 4)) return MOEQ_E_ALIGN;
   if (w->cols % 8) return MOEQ_E_SHAPE;
   if (T == 0) return MOEQ_OK;
+  if (mfma) {
+    LinearParams lp;
+    lp.w = static_cast<const uint8_t*>(w->data) + (size_t)expert * w->expert_stride;
+    lp.s = static_cast<const uint8_t*>(w->scales) + (size_t)expert * w->scale_expert_stride;
+    lp.x = static_cast<const uint16_t*>(x);
+    lp.y = y;
+    lp.rows = w->rows;
+    lp.cols = w->cols;
+    lp.T = T;
+    return hip_rc(launch_linear_fp8(lp, S(stream)));
+  }
   WsLayout lay;
   memset(&lay, 0, sizeof(lay));
   GemvParams p = gemv_params(nullptr, *w, nullptr, nullptr, lay);

@@ -103,6 +103,15 @@ struct PrefillParams {
   float* partial;        // down: [pairs][rows]
 };
 
+// Dense FP8 block-128 linear on the bf16 matrix instruction (two or more tokens).
+struct LinearParams {
+  const uint8_t* w;   // E4M3 codes [rows][cols] of one expert
+  const uint8_t* s;   // e8m0 [rows/128][cols/128]
+  const uint16_t* x;  // bf16 [T][cols], 16-byte aligned
+  float* y;           // fp32 [T][rows]
+  int rows, cols, T;
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int rows, int cols, int expert, float* out,
                           hipStream_t s);
@@ -122,6 +131,8 @@ hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s);
 bool fused1_supported(int fg, int fd, int hidden, int inter, int top_k);
 hipError_t launch_fused1(int fg, int fd, const FusedParams& p, hipStream_t s);
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int n_slots, hipStream_t s);
+bool linear_fp8_fits(int rows, int cols);  // rows % 128 == 0, cols % 256 == 0
+hipError_t launch_linear_fp8(const LinearParams& p, hipStream_t s);
 
 // Chunk geometry: weights per 16-byte chunk; lanes per row and chunks per lane.
 int weights_per_chunk(int fmt);

@@ -204,7 +204,13 @@ int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs,
                       int T, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Dense block-quantized linear y[T][rows] = W_expert x[T][cols] (fp32 out). Any
- * format; FP8_B128 is the dense-layer format (IQ2_XXS + Q2_K + FP8 hybrid card). */
+ * format; FP8_B128 is the dense-layer format (IQ2_XXS + Q2_K + FP8 hybrid card).
+ * x bf16 [T][cols], 16-byte aligned; y fp32 [T][rows], 4-byte aligned; both
+ * caller-owned, y overwritten. FP8_B128 with T >= 2 and cols a multiple of 256
+ * runs on the bf16 matrix instruction (E4M3 codes exact in bf16, block scale
+ * applied to each 128-wide K tile's fp32 partial); otherwise one GEMV pass per
+ * token group, which needs cols / (weights per 16-byte chunk) <= 256 (MOEQ_E_SHAPE
+ * beyond). Asynchronous on `stream`. */
 int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y, void* stream);
 
 /* MXFP8 quantisation of rows of K values (K a multiple of 32): per 32 consecutive

@@ -350,3 +350,26 @@ def test_linear_ragged(fmt, rows, cols):
         y = mq.linear(W, 0, x_tensor(x)).cpu().numpy()
         ref = moe.linear(formats.dequant(fmt, planes, rows, cols, scale2=1.25, grid=grid), x)
         assert rel_err(y, ref) < TOL, (fmt, T)
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 256), (384, 768), (256, 4608), (128, 8192)])
+def test_fp8_linear_token_batches(rows, cols):
+    """FP8 block-128 linear for T >= 2 (the matrix-instruction path): one K step,
+    fewer steps than waves, more steps than waves (4608 = 18 steps of 256 over 16
+    waves) and a long K; T spans a ragged single tile, several tiles and more than
+    one pass of four tiles over the weights. Expert 1 of two, so the expert offsets
+    are exercised; scale codes span 2^-27 .. 2^22."""
+    say("fp8 linear batches", rows, cols)
+    rng = np.random.default_rng(rows * 7 + cols)
+    planes = []
+    for e in range(2):
+        codes = synth.field_bytes(11 + e, 1, synth.FIELD_E4M3_FINITE, 0, rows * cols)
+        sc = rng.integers(100, 150, size=(rows // 128) * (cols // 128), dtype=np.uint8)
+        planes.append([codes, sc])
+    W = upload_weight(5, rows, cols, planes)
+    Wd = formats.dequant(5, planes[1], rows, cols)
+    for T in (2, 5, 16, 17, 64, 70):
+        x = synth.activations_bf16(int(rng.integers(1 << 30)), T, cols)
+        y = mq.linear(W, 1, x_tensor(x)).cpu().numpy()
+        ref = moe.linear(Wd, x)
+        assert rel_err(y, ref) < TOL, (rows, cols, T)
