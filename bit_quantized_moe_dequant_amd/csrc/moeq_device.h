@@ -5,7 +5,9 @@
 // lane) plus the chunk's scale side data, and offers:
 //   * dot<ACT>(chunk, side, xop, acc): acc + (decoded chunk) . (activation slice)
 //   * to_f32(chunk, side, out): the exact weights rounded once to fp32 (dequant)
-//   * load_x<ACT>(...): the activation slice in the register order dot() consumes.
+//   * load_x<ACT>(...): the activation slice in the register order dot() consumes,
+//     also as fetch_x (the loads only) and prep_x (the conversion), so a kernel can
+//     put its weight loads between the two.
 // Weights are expanded to bf16 pairs (exact for every format here: at most 8
 // significant bits before the block scale) and multiplied with v_dot2_f32_bf16;
 // the per-block scale is applied once per block to the fp32 partial sum.
@@ -79,21 +81,37 @@ __device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
 
 // -------------------------------------------------------------------------
 // Activation slices. XR<ACT>(n) = registers for n weights.
+// Every slice is read in two steps so that kernels can issue the loads early and
+// convert later: fetch<N> (the 16-byte loads, RawN<ACT, N>::V of them) and
+// from_raw<N> (register order for dot()); load<N> does both.
+template <int ACT, int N> struct RawN {
+  static constexpr int V = (ACT == ACT_BF16) ? N / 8 : N / 4;
+};
 template <int ACT> struct Act;
 template <> struct Act<ACT_BF16> {
   static constexpr int PER_PAIR = 1;
   // n contiguous bf16 values starting at element k0 of row p (n multiple of 8)
   template <int N>
-  __device__ static void load(const void* row, int k0, uint32_t* r) {
+  __device__ static void fetch(const void* row, int k0, u32x4* v) {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + k0;
 #pragma unroll
+    for (int i = 0; i < N / 8; i++) v[i] = ld16(p + 8 * i);
+  }
+  template <int N>
+  __device__ static void from_raw(const u32x4* v, uint32_t* r) {
+#pragma unroll
     for (int i = 0; i < N / 8; i++) {
-      u32x4 v = ld16(p + 8 * i);
-      r[4 * i + 0] = v[0];
-      r[4 * i + 1] = v[1];
-      r[4 * i + 2] = v[2];
-      r[4 * i + 3] = v[3];
+      r[4 * i + 0] = v[i][0];
+      r[4 * i + 1] = v[i][1];
+      r[4 * i + 2] = v[i][2];
+      r[4 * i + 3] = v[i][3];
     }
+  }
+  template <int N>
+  __device__ static void load(const void* row, int k0, uint32_t* r) {
+    u32x4 v[N / 8];
+    fetch<N>(row, k0, v);
+    from_raw<N>(v, r);
   }
   __device__ static float val(const void* row, int k) {
     uint32_t b = reinterpret_cast<const uint16_t*>(row)[k];
@@ -104,14 +122,24 @@ template <> struct Act<ACT_F32> {
   static constexpr int PER_PAIR = 2;
   // n contiguous fp32 values -> n/2 hi pairs then n/2 lo pairs
   template <int N>
-  __device__ static void load(const void* row, int k0, uint32_t* r) {
+  __device__ static void fetch(const void* row, int k0, u32x4* v) {
     const float* p = reinterpret_cast<const float*>(row) + k0;
 #pragma unroll
+    for (int i = 0; i < N / 4; i++) v[i] = ld16(p + 4 * i);
+  }
+  template <int N>
+  __device__ static void from_raw(const u32x4* v, uint32_t* r) {
+#pragma unroll
     for (int i = 0; i < N / 4; i++) {
-      u32x4 v = ld16(p + 4 * i);
-      split_pair(u2f(v[0]), u2f(v[1]), r[2 * i], r[N / 2 + 2 * i]);
-      split_pair(u2f(v[2]), u2f(v[3]), r[2 * i + 1], r[N / 2 + 2 * i + 1]);
+      split_pair(u2f(v[i][0]), u2f(v[i][1]), r[2 * i], r[N / 2 + 2 * i]);
+      split_pair(u2f(v[i][2]), u2f(v[i][3]), r[2 * i + 1], r[N / 2 + 2 * i + 1]);
     }
+  }
+  template <int N>
+  __device__ static void load(const void* row, int k0, uint32_t* r) {
+    u32x4 v[N / 4];
+    fetch<N>(row, k0, v);
+    from_raw<N>(v, r);
   }
   __device__ static float val(const void* row, int k) { return reinterpret_cast<const float*>(row)[k]; }
 };
@@ -120,14 +148,20 @@ template <> struct Act<ACT_F32_COHERENT> {
   static constexpr int PER_PAIR = 2;
   // n contiguous fp32 values -> n/2 hi pairs then n/2 lo pairs
   template <int N>
-  __device__ static void load(const void* row, int k0, uint32_t* r) {
+  __device__ static void fetch(const void* row, int k0, u32x4* v) {
     const float* p = reinterpret_cast<const float*>(row) + k0;
 #pragma unroll
-    for (int i = 0; i < N / 4; i++) {
-      u32x4 v = ld16_coherent(p + 4 * i);
-      split_pair(u2f(v[0]), u2f(v[1]), r[2 * i], r[N / 2 + 2 * i]);
-      split_pair(u2f(v[2]), u2f(v[3]), r[2 * i + 1], r[N / 2 + 2 * i + 1]);
-    }
+    for (int i = 0; i < N / 4; i++) v[i] = ld16_coherent(p + 4 * i);
+  }
+  template <int N>
+  __device__ static void from_raw(const u32x4* v, uint32_t* r) {
+    Act<ACT_F32>::template from_raw<N>(v, r);
+  }
+  template <int N>
+  __device__ static void load(const void* row, int k0, uint32_t* r) {
+    u32x4 v[N / 4];
+    fetch<N>(row, k0, v);
+    from_raw<N>(v, r);
   }
   __device__ static float val(const void* row, int k) { return reinterpret_cast<const float*>(row)[k]; }
 };
@@ -165,7 +199,15 @@ template <> struct Dec<FMT_MXFP4> {
   template <int ACT>
   __device__ static int xregs() { return 16 * Act<ACT>::PER_PAIR; }
   template <int ACT>
-  __device__ static void load_x(const void* row, int ch, uint32_t* x, float* /*xs*/) {
+  __device__ static void fetch_x(const void* row, int ch, u32x4* raw) {
+    Act<ACT>::template fetch<32>(row, ch * 32, raw);
+  }
+  template <int ACT>
+  __device__ static void prep_x(const u32x4* raw, uint32_t* x, float*) {
+    Act<ACT>::template from_raw<32>(raw, x);
+  }
+  template <int ACT>
+  __device__ static void load_x(const void* row, int ch, uint32_t* x, float*) {
     Act<ACT>::template load<32>(row, ch * 32, x);
   }
   template <int ACT>
@@ -216,6 +258,14 @@ template <> struct Dec<FMT_NVFP4> {
   }
   __device__ static const uint8_t* chunk_ptr(const WView& w, int r, int ch) {
     return w.data + (size_t)r * (w.cols / 2) + (size_t)ch * 16;
+  }
+  template <int ACT>
+  __device__ static void fetch_x(const void* row, int ch, u32x4* raw) {
+    Act<ACT>::template fetch<32>(row, ch * 32, raw);
+  }
+  template <int ACT>
+  __device__ static void prep_x(const u32x4* raw, uint32_t* x, float*) {
+    Act<ACT>::template from_raw<32>(raw, x);
   }
   template <int ACT>
   __device__ static void load_x(const void* row, int ch, uint32_t* x, float*) {
@@ -293,38 +343,45 @@ template <> struct Dec<FMT_Q2_K> {
   // x layout: for p < 4, i < 4: pair A (bytes 0,2 of word i) at 8p + 2i, pair B
   // (bytes 1,3) at 8p + 2i + 1. xs[p] = sum of the 16 activations of sub-block p.
   template <int ACT>
-  __device__ static void load_x(const void* row, int ch, uint32_t* x, float* xs) {
+  __device__ static void fetch_x(const void* row, int ch, u32x4* raw) {
+    constexpr int R = RawN<ACT, 16>::V;
+#pragma unroll
+    for (int p = 0; p < 4; p++) Act<ACT>::template fetch<16>(row, seg_base(ch, p), raw + R * p);
+  }
+  template <int ACT>
+  __device__ static void prep_x(const u32x4* raw, uint32_t* x, float* xs) {
+    constexpr int R = RawN<ACT, 16>::V;
 #pragma unroll
     for (int p = 0; p < 4; p++) {
-      int k0 = seg_base(ch, p);
+      const u32x4* v = raw + R * p;
+      float s = 0.f;
       if (ACT == ACT_BF16) {
-        uint32_t r8[8];
-        Act<ACT_BF16>::template load<16>(row, k0, r8);
-        float s = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          uint32_t w0 = r8[2 * i], w1 = r8[2 * i + 1];  // (x0,x1), (x2,x3)
-          x[8 * p + 2 * i] = (w0 & 0xFFFFu) | (w1 << 16);          // (x0, x2)
-          x[8 * p + 2 * i + 1] = (w0 >> 16) | (w1 & 0xFFFF0000u);  // (x1, x3)
+          uint32_t w0 = v[i >> 1][2 * (i & 1)], w1 = v[i >> 1][2 * (i & 1) + 1];  // (x0,x1), (x2,x3)
+          x[8 * p + 2 * i] = (w0 & 0xFFFFu) | (w1 << 16);                           // (x0, x2)
+          x[8 * p + 2 * i + 1] = (w0 >> 16) | (w1 & 0xFFFF0000u);                   // (x1, x3)
           s += __builtin_bit_cast(float, w0 << 16) + __builtin_bit_cast(float, w0 & 0xFFFF0000u) +
                __builtin_bit_cast(float, w1 << 16) + __builtin_bit_cast(float, w1 & 0xFFFF0000u);
         }
-        xs[p] = s;
       } else {
-        const float* f = reinterpret_cast<const float*>(row) + k0;
-        float s = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          u32x4 v = ACT == ACT_F32_COHERENT ? ld16_coherent(f + 4 * i) : ld16(f + 4 * i);
-          float x0 = u2f(v[0]), x1 = u2f(v[1]);
-          float x2 = u2f(v[2]), x3 = u2f(v[3]);
+          float x0 = u2f(v[i][0]), x1 = u2f(v[i][1]);
+          float x2 = u2f(v[i][2]), x3 = u2f(v[i][3]);
           split_pair(x0, x2, x[8 * p + 2 * i], x[32 + 8 * p + 2 * i]);
           split_pair(x1, x3, x[8 * p + 2 * i + 1], x[32 + 8 * p + 2 * i + 1]);
           s += (x0 + x1) + (x2 + x3);
         }
-        xs[p] = s;
       }
+      xs[p] = s;
     }
+  }
+  template <int ACT>
+  __device__ static void load_x(const void* row, int ch, uint32_t* x, float* xs) {
+    u32x4 raw[4 * RawN<ACT, 16>::V];
+    fetch_x<ACT>(row, ch, raw);
+    prep_x<ACT>(raw, x, xs);
   }
   template <int ACT>
   __device__ static float dot(u32x4 q, Side s, const uint32_t* x, const float* xs, float acc, const Iq2Lds*) {
@@ -406,6 +463,14 @@ template <> struct Dec<FMT_IQ2_XXS> {
     return w.data + (size_t)r * (w.cols / 256) * 64 + (size_t)ch * 16;
   }
   template <int ACT>
+  __device__ static void fetch_x(const void* row, int ch, u32x4* raw) {
+    Act<ACT>::template fetch<64>(row, ch * 64, raw);
+  }
+  template <int ACT>
+  __device__ static void prep_x(const u32x4* raw, uint32_t* x, float*) {
+    Act<ACT>::template from_raw<64>(raw, x);
+  }
+  template <int ACT>
   __device__ static void load_x(const void* row, int ch, uint32_t* x, float*) {
     Act<ACT>::template load<64>(row, ch * 64, x);
   }
@@ -465,6 +530,14 @@ template <> struct Dec<FMT_FP8_B128> {
     return w.data + (size_t)r * w.cols + (size_t)ch * 16;
   }
   template <int ACT>
+  __device__ static void fetch_x(const void* row, int ch, u32x4* raw) {
+    Act<ACT>::template fetch<16>(row, ch * 16, raw);
+  }
+  template <int ACT>
+  __device__ static void prep_x(const u32x4* raw, uint32_t* x, float*) {
+    Act<ACT>::template from_raw<16>(raw, x);
+  }
+  template <int ACT>
   __device__ static void load_x(const void* row, int ch, uint32_t* x, float*) {
     Act<ACT>::template load<16>(row, ch * 16, x);
   }
@@ -500,6 +573,10 @@ template <> struct Dec<FMT_FP8_B128> {
 };
 
 // Registers of one chunk's activation slice for a format and activation kind.
+// 16-byte loads behind one chunk's activation slice (fetch_x / prep_x).
+template <int FMT, int ACT> struct XRaw {
+  static constexpr int N = RawN<ACT, Dec<FMT>::WPC>::V;
+};
 template <int FMT, int ACT> struct XRegs {
   static constexpr int N = Dec<FMT>::WPC / 2 * (ACT != ACT_BF16 ? 2 : 1);
   static constexpr int NS = (FMT == FMT_Q2_K) ? 4 : 1;

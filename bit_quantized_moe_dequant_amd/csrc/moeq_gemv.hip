@@ -54,8 +54,11 @@ __global__ __launch_bounds__(256) void k_dequant(WeightRef w, const uint8_t* gri
 }
 
 // ---------------------------------------------------------------- GEMV
+#ifndef MOEQ_GEMV_WPE
+#define MOEQ_GEMV_WPE 2  // waves per SIMD the register budget must allow
+#endif
 template <int FMT, int CPL, int MT, int NMAT, int EPI, int ACT, int UB, int NB>
-__global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOEQ_GEMV_WPE))) void k_gemv(GemvParams P) {
   using D = Dec<FMT>;
   typedef typename D::Side Side;
   constexpr int XN = XRegs<FMT, ACT>::N;
@@ -115,35 +118,64 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
 #pragma unroll
   for (int mt = 0; mt < NMAT; mt++) s2[mt] = (FMT == FMT_NVFP4) ? P.w[mt].scale2[e] : 1.0f;
 
+  constexpr int XR = XRaw<FMT, ACT>::N;
   for (int m0 = 0; m0 < M; m0 += MT) {
+    // Loads go out in the order they are needed, all before any arithmetic: the
+    // activation slices of the tile's tokens, then the weight rows batch by batch.
+    // They complete in issue order, so the first batch's arithmetic overlaps the
+    // later batches' transfer. Every load is unconditional: tokens past the
+    // expert's last re-read its last token, rows and chunks past the end the last
+    // valid one; their results are masked.
+    u32x4 xraw[MT][CPL][XR];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) {
+      const int m = min(m0 + mi, M - 1);
+      const int pair = (P.mode == MODE_DIRECT) ? slot : (P.mode == MODE_GROUPED ? P.route.perm()[pstart + m] : m);
+      const void* row;
+      if (ACT == ACT_BF16) {
+        const int tok = (P.mode == MODE_LINEAR) ? m : pair / P.top_k;
+        row = reinterpret_cast<const uint16_t*>(P.act) + (size_t)tok * P.cols;
+      } else {
+        row = reinterpret_cast<const float*>(P.act) + (size_t)pair * P.cols;
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; c++) D::template fetch_x<ACT>(row, min(lr + lpr * c, P.chunks - 1), xraw[mi][c]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 q[NB][NMAT][UB][CPL];
+    Side sd[NB][NMAT][UB][CPL];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int mt = 0; mt < NMAT; mt++)
+#pragma unroll
+        for (int ub = 0; ub < UB; ub++) {
+          const int r = min(wr0 + (nb * UB + ub) * rw_rows + rsub, P.rows - 1);
+#pragma unroll
+          for (int c = 0; c < CPL; c++) {
+            const int ch = min(lr + lpr * c, P.chunks - 1);
+            q[nb][mt][ub][c] = ld16(D::chunk_ptr(W[mt], r, ch));
+            sd[nb][mt][ub][c] = D::side(W[mt], r, ch);
+          }
+        }
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t x[MT][CPL][XN];
     float xs[MT][CPL][XS];
 #pragma unroll
-    for (int mi = 0; mi < MT; mi++) {
-      const int m = m0 + mi;
-      if (m < M) {
-        int pair = (P.mode == MODE_DIRECT) ? slot : (P.mode == MODE_GROUPED ? P.route.perm()[pstart + m] : m);
-        const void* row;
-        if (ACT == ACT_BF16) {
-          int tok = (P.mode == MODE_LINEAR) ? m : pair / P.top_k;
-          row = reinterpret_cast<const uint16_t*>(P.act) + (size_t)tok * P.cols;
-        } else {
-          row = reinterpret_cast<const float*>(P.act) + (size_t)pair * P.cols;
-        }
+    for (int mi = 0; mi < MT; mi++)
 #pragma unroll
-        for (int c = 0; c < CPL; c++) {
-          if (lr + lpr * c < P.chunks) {
-            D::template load_x<ACT>(row, lr + lpr * c, x[mi][c], xs[mi][c]);
-          } else {
+      for (int c = 0; c < CPL; c++) D::template prep_x<ACT>(xraw[mi][c], x[mi][c], xs[mi][c]);
+    // Chunks past the row end contribute nothing: both operands are zeroed, the
+    // activations here and the weights where they are used (a NaN code times a
+    // zero activation would still be NaN; overwriting a load's destination here
+    // would have to wait for the load).
+    bool cvalid[CPL];
 #pragma unroll
-            for (int j = 0; j < XN; j++) x[mi][c][j] = 0u;
+    for (int c = 0; c < CPL; c++) {
+      cvalid[c] = lr + lpr * c < P.chunks;
+      if (!cvalid[c]) {
 #pragma unroll
-            for (int j = 0; j < XS; j++) xs[mi][c][j] = 0.f;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
+        for (int mi = 0; mi < MT; mi++) {
 #pragma unroll
           for (int j = 0; j < XN; j++) x[mi][c][j] = 0u;
 #pragma unroll
@@ -155,24 +187,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       const int u0 = nb * UB;
-      u32x4 q[NMAT][UB][CPL];
-      Side sd[NMAT][UB][CPL];
-#pragma unroll
-      for (int mt = 0; mt < NMAT; mt++)
-#pragma unroll
-        for (int ub = 0; ub < UB; ub++) {
-          const int r = wr0 + (u0 + ub) * rw_rows + rsub;
-#pragma unroll
-          for (int c = 0; c < CPL; c++) {
-            if (r < P.rows && lr + lpr * c < P.chunks) {
-              q[mt][ub][c] = ld16(D::chunk_ptr(W[mt], r, lr + lpr * c));
-              sd[mt][ub][c] = D::side(W[mt], r, lr + lpr * c);
-            } else {
-              q[mt][ub][c] = u32x4{0u, 0u, 0u, 0u};
-              sd[mt][ub][c] = Side{};
-            }
-          }
-        }
       float acc[NMAT][NV];
 #pragma unroll
       for (int mt = 0; mt < NMAT; mt++)
@@ -183,7 +197,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
             float a = 0.f;
 #pragma unroll
             for (int c = 0; c < CPL; c++)
-              a = D::template dot<ACT>(q[mt][ub][c], sd[mt][ub][c], x[mi][c], xs[mi][c], a, &lds_tab[0]);
+              a = D::template dot<ACT>(cvalid[c] ? q[nb][mt][ub][c] : u32x4{0u, 0u, 0u, 0u},
+                                       cvalid[c] ? sd[nb][mt][ub][c] : Side{}, x[mi][c], xs[mi][c], a, &lds_tab[0]);
             acc[mt][ub * MT + mi] = a;
           }
 #pragma unroll
@@ -221,17 +236,21 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
 }
 
 // ---------------------------------------------------------------- down for one token
-template <int FMT, int CPL, int UB, int NB>
-__global__ __launch_bounds__(1024) void k_down1(Down1Params P) {
+// One wave per routed slot (top_k <= MAXW). The bound on the work-group size sets
+// the register budget: MAXW = 8 leaves 256 VGPRs, enough to keep every load of a
+// wave in flight for every format; MAXW = 16 leaves 128.
+template <int FMT, int CPL, int UB, int NB, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void k_down1(Down1Params P) {
   using D = Dec<FMT>;
   typedef typename D::Side Side;
   constexpr int XN = XRegs<FMT, ACT_F32>::N;
   constexpr int XS = XRegs<FMT, ACT_F32>::NS;
   __shared__ Iq2Lds lds_tab[1];
-  __shared__ float red[16][64];
+  __shared__ float red[MAXW][64];
 
   const int lane = threadIdx.x & 63;
-  const int k = threadIdx.x >> 6;  // slot handled by this wave
+  // Slot handled by this wave; uniform, so its expert id is a scalar load.
+  const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lpr = P.lpr;
   const int rw_rows = 64 / lpr;
   const int lr = lane & (lpr - 1);
@@ -250,14 +269,45 @@ __global__ __launch_bounds__(1024) void k_down1(Down1Params P) {
     WView W = expert_view<FMT>(P.w, e, P.rows, P.cols);
     const float s2 = (FMT == FMT_NVFP4) ? P.w.scale2[e] : 1.0f;
     const float wk = P.rw[k] * s2;
+    // Loads go out in the order they are needed, all before any arithmetic: the h
+    // slice, then the weights batch by batch. They complete in issue order, so the
+    // first batch's arithmetic overlaps the later batches' transfer instead of
+    // waiting for the wave's last byte. Every load is unconditional: rows and
+    // chunks past the end re-read the last valid one and are masked afterwards.
+    constexpr int XR = XRaw<FMT, ACT_F32>::N;
+    const float* hrow = P.h + (size_t)k * P.cols;
+    u32x4 hraw[CPL][XR];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) D::template fetch_x<ACT_F32>(hrow, min(lr + lpr * c, P.chunks - 1), hraw[c]);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 q[NB][UB][CPL];
+    Side sd[NB][UB][CPL];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int ub = 0; ub < UB; ub++) {
+        const int r = min(tile_r0 + (nb * UB + ub) * rw_rows + rsub, P.rows - 1);
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          const int ch = min(lr + lpr * c, P.chunks - 1);
+          q[nb][ub][c] = ld16(D::chunk_ptr(W, r, ch));
+          sd[nb][ub][c] = D::side(W, r, ch);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t x[CPL][XN];
     float xs[CPL][XS];
-    const float* hrow = P.h + (size_t)k * P.cols;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) D::template prep_x<ACT_F32>(hraw[c], x[c], xs[c]);
+    // Chunks past the row end contribute nothing: both operands are zeroed, the
+    // activations here and the weights where they are used (a NaN code times a
+    // zero activation would still be NaN; overwriting a load's destination here
+    // would have to wait for the load).
+    bool cvalid[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
-      if (lr + lpr * c < P.chunks) {
-        D::template load_x<ACT_F32>(hrow, lr + lpr * c, x[c], xs[c]);
-      } else {
+      cvalid[c] = lr + lpr * c < P.chunks;
+      if (!cvalid[c]) {
 #pragma unroll
         for (int j = 0; j < XN; j++) x[c][j] = 0u;
 #pragma unroll
@@ -267,28 +317,14 @@ __global__ __launch_bounds__(1024) void k_down1(Down1Params P) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       const int u0 = nb * UB;
-      u32x4 q[UB][CPL];
-      Side sd[UB][CPL];
-#pragma unroll
-      for (int ub = 0; ub < UB; ub++) {
-        const int r = tile_r0 + (u0 + ub) * rw_rows + rsub;
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
-          if (r < P.rows && u0 + ub < P.U && lr + lpr * c < P.chunks) {
-            q[ub][c] = ld16(D::chunk_ptr(W, r, lr + lpr * c));
-            sd[ub][c] = D::side(W, r, lr + lpr * c);
-          } else {
-            q[ub][c] = u32x4{0u, 0u, 0u, 0u};
-            sd[ub][c] = Side{};
-          }
-        }
-      }
       float acc[UB];
 #pragma unroll
       for (int ub = 0; ub < UB; ub++) {
         float a = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; c++) a = D::template dot<ACT_F32>(q[ub][c], sd[ub][c], x[c], xs[c], a, &lds_tab[0]);
+        for (int c = 0; c < CPL; c++)
+          a = D::template dot<ACT_F32>(cvalid[c] ? q[nb][ub][c] : u32x4{0u, 0u, 0u, 0u},
+                                       cvalid[c] ? sd[nb][ub][c] : Side{}, x[c], xs[c], a, &lds_tab[0]);
         acc[ub] = a;
       }
       group_reduce<UB>(acc, lpr, lane);
@@ -367,13 +403,19 @@ hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int 
   return hipGetLastError();
 }
 
+#ifndef MOEQ_GEMV_UB
+#define MOEQ_GEMV_UB 4  // rows per batch (gate/up, linear, grouped down)
+#endif
 #ifndef MOEQ_GEMV_NB
-#define MOEQ_GEMV_NB 1  // row batches of 4 per wave (gate/up, linear, grouped down)
+#define MOEQ_GEMV_NB 1  // row batches per wave (gate/up, linear, grouped down)
+#endif
+#ifndef MOEQ_DOWN1_UB
+#define MOEQ_DOWN1_UB 4  // rows per batch (single-token down)
 #endif
 #ifndef MOEQ_DOWN1_NB
-#define MOEQ_DOWN1_NB 2  // row batches of 4 per wave (single-token down)
+#define MOEQ_DOWN1_NB 2  // row batches per wave (single-token down)
 #endif
-constexpr int GEMV_UB = 4, GEMV_NB = MOEQ_GEMV_NB, DOWN1_UB = 4, DOWN1_NB = MOEQ_DOWN1_NB;
+constexpr int GEMV_UB = MOEQ_GEMV_UB, GEMV_NB = MOEQ_GEMV_NB, DOWN1_UB = MOEQ_DOWN1_UB, DOWN1_NB = MOEQ_DOWN1_NB;
 
 // Launch with hipExtLaunchKernelGGL when timing events are given: the events
 // then bracket the kernel's execution itself, not the queue around it.
@@ -383,10 +425,19 @@ constexpr int GEMV_UB = 4, GEMV_NB = MOEQ_GEMV_NB, DOWN1_UB = 4, DOWN1_NB = MOEQ
     else hipLaunchKernelGGL(K, g, b, 0, s, p);                                        \
   } while (0)
 
+// IQ2_XXS decodes at several times the ALU cost per byte of the other formats: its
+// four rows go in two batches of two, so the first batch's arithmetic overlaps
+// the second's transfer; the cheaper formats do better with one batch of four.
+template <int FMT> struct GemvRows {
+  static constexpr int UB = FMT == FMT_IQ2_XXS ? 2 : GEMV_UB;
+  static constexpr int NB = FMT == FMT_IQ2_XXS ? 2 : GEMV_NB;
+  static_assert(UB * NB == GEMV_UB * GEMV_NB, "rows per wave must not depend on the format");
+};
+
 template <int FMT, int CPL>
 static hipError_t gemv_fc(int epi, const GemvParams& p, dim3 g, int mt, hipStream_t s, const LaunchEvents* ev) {
   dim3 b(256);
-  constexpr int UB = GEMV_UB, NB = GEMV_NB;
+  constexpr int UB = GemvRows<FMT>::UB, NB = GemvRows<FMT>::NB;
   if (epi == EPI_SWIGLU) {
     if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
     else MOEQ_LAUNCH((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
@@ -432,16 +483,21 @@ hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int m
   return hipErrorInvalidValue;
 }
 
-template <int FMT>
-static hipError_t down1_f(const Down1Params& p, int cpl, dim3 g, dim3 b, hipStream_t s) {
+template <int FMT, int MAXW>
+static hipError_t down1_fw(const Down1Params& p, int cpl, dim3 g, dim3 b, hipStream_t s) {
   constexpr int UB = DOWN1_UB, NB = DOWN1_NB;
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((k_down1<FMT, 1, UB, NB>), g, b, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_down1<FMT, 2, UB, NB>), g, b, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_down1<FMT, 4, UB, NB>), g, b, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_down1<FMT, 1, UB, NB, MAXW>), g, b, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_down1<FMT, 2, UB, NB, MAXW>), g, b, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_down1<FMT, 4, UB, NB, MAXW>), g, b, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t down1_f(const Down1Params& p, int cpl, dim3 g, dim3 b, hipStream_t s) {
+  return p.top_k <= 8 ? down1_fw<FMT, 8>(p, cpl, g, b, s) : down1_fw<FMT, 16>(p, cpl, g, b, s);
 }
 
 hipError_t launch_down1(int fmt, const Down1Params& p, hipStream_t s) {
