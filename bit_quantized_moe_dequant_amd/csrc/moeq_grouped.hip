@@ -1,0 +1,209 @@
+// Token-grouped gate/up for IQ2_XXS experts on the bf16 matrix instruction
+// v_mfma_f32_16x16x32_bf16, for batches (T > 1) routed through the grouping tables.
+//
+// The GEMV path decodes an expert's weights once per routed token; this kernel
+// decodes them once per group of up to 16 tokens and lets the matrix instruction
+// do the multiply-adds. IQ2_XXS decodes exactly into bf16: a codebook entry is
+// eight small integers (at most 8 significant bits) and a sign per entry (IQ2_XXS
+// + Q2_K + FP8 hybrid card, format table; the block layout of IQ2_XXS: sub-blocks
+// of 32 weights, four 8-weight groups each, a 4-bit scale per sub-block and an
+// fp16 d per 256). The sub-block scale multiplies the instruction's fp32 partial,
+// so, as in the GEMV, only the fp32 accumulation rounds.
+//
+// Instruction operands: the weights are operand B (16 columns = 16 weight rows),
+// the tokens operand A (16 rows = up to 16 tokens of the expert). One instruction
+// covers one sub-block (K = 32) of 16 weight rows: lane (n = lane % 16, g = lane /
+// 16) supplies group g of row n's sub-block (its 8 weights as four bf16 pairs) and,
+// for operand A, the 8 activations of token n at the same K. Output lane L
+// register r is token 4(L/16) + r, weight row L % 16: the lane that decoded row n
+// also holds row n's outputs, so it scales them with the sub-block scale it
+// decoded itself.
+//
+// Work: a work-group is (one routed expert, 64 weight rows); each of its four waves
+// takes 16 rows of the gate and of the up matrix (SwiGLU is then lane-local).
+// Superblocks (256 K) stream through two register buffers: the next superblock's
+// loads are issued before the current one is computed. The decode is bound by
+// VALU and by the random 16-byte codebook reads from LDS together (four waves per
+// SIMD with half-superblock buffers ran slower than two with whole ones). Token lanes past the
+// expert's last token read that token again (same addresses) and are not stored.
+#include <hip/hip_runtime.h>
+
+#include "moeq_device.h"
+#include "moeq_kernels.h"
+
+namespace moeq {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int GI_WAVES = 4;
+constexpr int GI_ROWS = 16 * GI_WAVES;  // weight rows per work-group
+
+// One superblock (256 K) of one wave: the 64 bytes of sub-block data and the fp16
+// d of row n for both matrices, and the 16-token activation slices (8 bf16 per
+// sub-block per lane).
+struct GiBuf {
+  u32x4 w[2][4];
+  uint32_t d[2];
+  u32x4 x[8];
+};
+
+// Raw buffer loads: a uniform base (the expert's planes, the activations), a
+// loop-invariant lane offset and a uniform superblock offset, so the loop needs no
+// per-lane address registers (whose reuse made the compiler wait for loads still
+// in flight).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gi_buffer(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+struct GiStreams {
+  __amdgpu_buffer_rsrc_t w[2], s[2], x;
+  int w_off, s_off, x_off;  // lane byte offsets: row rn's data and d, token row + group g
+};
+
+// Loads of superblock sb of row n (and of the token's activations at the same K).
+__device__ __forceinline__ void gi_issue(const GiStreams& st, int sb, GiBuf& b) {
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      b.w[mt][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.w[mt], st.w_off + 16 * i, sb * 64, 0));
+    b.d[mt] = __builtin_amdgcn_raw_buffer_load_b16(st.s[mt], st.s_off, sb * 2, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++)
+    b.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, st.x_off + 64 * j, sb * 512, 0));
+}
+
+// The four sign words of every 7-bit sign code (iq2_sign_words), looked up per
+// group: one LDS read in place of about a dozen VALU operations.
+struct GiSigns {
+  u32x4 w[128];
+};
+
+__device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* t, const GiSigns* sg,
+                                           f32x4_t (&acc)[2]) {
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    const float d8 = half_bits_f32(b.d[mt]) * 0.125f;
+    f32x4_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t a0 = b.w[mt][j >> 1][2 * (j & 1)], a1 = b.w[mt][j >> 1][2 * (j & 1) + 1];
+      const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
+      const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
+      const u32x4 m = sg->w[code];
+      // sign bits of the codebook words are clear, so OR applies the signs
+      const u32x4 wv = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
+      c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.x[j]),
+                                                     __builtin_bit_cast(bf16x8_t, wv), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0,
+                                                     0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t a1 = b.w[mt][j >> 1][2 * (j & 1) + 1];
+      const float db = d8 * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
+#pragma unroll
+      for (int r = 0; r < 4; r++) acc[mt][r] = __builtin_fmaf(c[j][r], db, acc[mt][r]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_gu_iq2(GemvParams P) {
+  __shared__ Iq2Lds lds_tab[1];
+  __shared__ GiSigns signs[1];
+  iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
+  if (threadIdx.x < 128) {
+    uint32_t m[4];
+    iq2_sign_words(threadIdx.x, m);
+    signs[0].w[threadIdx.x] = u32x4{m[0], m[1], m[2], m[3]};
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int slot = blockIdx.y;
+  if (slot >= P.route.n_slots()[0]) return;
+  const int e = P.route.slots()[slot];
+  const int pstart = P.route.offsets()[e];
+  const int M = P.route.offsets()[e + 1] - pstart;
+  const int n0 = blockIdx.x * GI_ROWS + wave * 16;
+  if (n0 >= P.rows || M <= 0) return;
+
+  if (e < 0 || e >= P.n_experts) {
+    // Out-of-range expert id (its bucket): its pairs contribute nothing.
+    for (int m = 0; m < M; m++) {
+      const int pair = P.route.perm()[pstart + m];
+      if (lane < 16 && n0 + lane < P.rows) P.out[(size_t)pair * P.rows + n0 + lane] = 0.f;
+    }
+    return;
+  }
+
+  const int nsb = P.cols / 256;
+  const int rn = min(n0 + n, P.rows - 1);
+  GiStreams st;
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    st.w[mt] = gi_buffer(P.w[mt].data + (size_t)e * P.w[mt].estride);
+    st.s[mt] = gi_buffer(P.w[mt].scales + (size_t)e * P.w[mt].sestride);
+  }
+  st.x = gi_buffer(P.act);
+  st.w_off = rn * nsb * 64;
+  st.s_off = rn * nsb * 2;
+
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    // Token of operand-A row n (lanes past the last token repeat it).
+    const int pa = P.route.perm()[pstart + min(m0 + n, M - 1)];
+    st.x_off = (pa / P.top_k) * P.cols * 2 + 16 * g;
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    GiBuf A, B;
+    gi_issue(st, 0, A);
+    // Two buffers in turn; the prefetch is unconditional (after the last
+    // superblock it re-reads it, a cache hit), so no branch separates a prefetch
+    // from the arithmetic after it.
+    for (int sb = 0;; sb += 2) {
+      gi_issue(st, min(sb + 1, nsb - 1), B);
+      __builtin_amdgcn_sched_barrier(0);
+      gi_compute(A, g, &lds_tab[0], &signs[0], acc);
+      if (sb + 1 >= nsb) break;
+      gi_issue(st, min(sb + 2, nsb - 1), A);
+      __builtin_amdgcn_sched_barrier(0);
+      gi_compute(B, g, &lds_tab[0], &signs[0], acc);
+      if (sb + 2 >= nsb) break;
+    }
+    // The final prefetch is never used: let it land before the registers are reused.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Lane: weight row n0 + n, tokens m0 + 4g + r.
+    if (n0 + n < P.rows) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = m0 + 4 * g + r;
+        if (m < M) {
+          const int pair = P.route.perm()[pstart + m];
+          P.out[(size_t)pair * P.rows + n0 + n] = silu_mul(acc[0][r], acc[1][r]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Buffer offsets are 32-bit: an expert's data plane and the activations must stay
+// under 2^31 bytes (T * cols * 2 is checked at launch).
+bool gu_iq2_fits(int rows, int cols) {
+  return rows > 0 && cols > 0 && cols % 256 == 0 && (long)rows * (cols / 256) * 64 < (1L << 31);
+}
+
+hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, hipStream_t s) {
+  if (!gu_iq2_fits(p.rows, p.cols) || (long)p.T * p.cols * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  dim3 g((unsigned)((p.rows + GI_ROWS - 1) / GI_ROWS), (unsigned)n_slots);
+  hipLaunchKernelGGL(k_gu_iq2, g, dim3(64 * GI_WAVES), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moeq

@@ -214,6 +214,34 @@ def test_forward_small_layers(case, T):
     assert rel_err(y, y2) < 1e-5          # one-launch layer vs the stage kernels
 
 
+@pytest.mark.parametrize("T,I", [(40, 224), (7, 64)])
+def test_iq2_grouped_gate_up(T, I):
+    """IQ2_XXS gate/up for T > 1 (the matrix-instruction path): with two experts and
+    top-2 every expert gets all T tokens, so T = 40 spans three 16-token tiles;
+    I = 224 leaves the last 64-row work-group half empty; one out-of-range id puts
+    a pair in the invalid bucket, whose h must be zero."""
+    say("iq2 grouped", T, I)
+    spec = workloads.LayerSpec(512, I, 2, 2, mq.FMT_IQ2_XXS, mq.FMT_MXFP4, seed=4400 + T)
+    layer = upload_layer(spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, 2, 2)
+    ids = ids.copy()
+    ids[1, 0] = 99
+    x = synth.activations_bf16(spec.seed + 1, T, 512)
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    it = cuda(ids)
+    mq.route(layer, it, ws=ws)
+    h = mq.gate_up(layer, x_tensor(x), it, ws=ws).cpu().numpy().reshape(T, 2, I)
+    assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    assert np.all(h[1, 0] == 0.0)
+    ids2 = ids.copy()
+    ids2[1, 0] = 0
+    _, ref_h = moe.moe_layer(x, ids2, rw, oracle_weight_fn(spec))
+    ok = np.ones((T, 2), bool)
+    ok[1, 0] = False
+    assert rel_err(h[ok], ref_h[ok]) < TOL
+
+
 def test_one_launch_layer_repeats_exactly():
     """The single-token layer runs as one work-queue launch whose counters reset at
     the end of each launch: many launches in a row must give identical results."""
