@@ -44,15 +44,23 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    """Digest of the kernel sources a traffic measurement belongs to."""
+# Sources the dominant kernel of each workload is built from (its own file and the
+# shared headers): a traffic measurement stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "mxfp4_layer": ("moeq_gemv.hip", "moeq_device.h", "moeq_kernels.h"),
+    "prefill_mxfp4": ("moeq_prefill.hip", "moeq_device.h", "moeq_kernels.h"),
+}
+
+
+def source_digest(workload: str) -> str:
+    """Digest of the kernel sources a traffic measurement of `workload` belongs to."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_moe_dequant_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    names = KERNEL_SOURCES.get(workload) or sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h")))
+    for name in sorted(names):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -64,7 +72,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_digest") != source_digest():
+    if t.get("source_digest") != source_digest(workload):
         return None
     return t.get("hbm_bytes_per_launch")
 
