@@ -1,0 +1,214 @@
+// Single-token gate/up + SwiGLU for MXFP4 experts on the block-scaled matrix
+// instruction v_mfma_scale_f32_16x16x128_f8f6f4, with no weight decode on the VALU.
+//
+// The MXFP4 weights (e2m1 codes, one e8m0 scale per 32 along K: DeepSeek-V4-Flash
+// W4A16-FP8 model card, "Architecture & precision") are the instruction's FP4
+// operand B as they sit in memory: lane (row n, group g) passes the 16-byte chunk
+// of its row at K = 32g + [0, 32) and that chunk's e8m0 as its B scale. The bf16
+// token is operand A, split into two E4M3 terms, x = hi + lo, each with an e8m0
+// scale per 32: hi holds the top four significant bits of every value and lo the
+// rest (a bf16 value has eight), so the split is exact except for values more than
+// 2^12 below their block's maximum, which lose low bits below 2^-16 of that
+// maximum. The products run at the FP8 rate in the matrix unit and accumulate in
+// fp32; the VALU only converts x, once per work-group. (Decoding FP4 on the VALU,
+// where v_cvt_scalef32_pk_bf16_fp4 issues at half rate, cost about as many cycles
+// per weight as the weight stream itself.)
+//
+// Instruction layout (pinned on the device): B lane L = column L % 16 (a weight
+// row) with K = 32(L/16) + [0, 32), low nibble first; A lane L = row L % 16 with
+// bytes 0-15 at K = 16(L/16) + [0, 16) and bytes 16-31 at K = 64 + 16(L/16) +
+// [0, 16); the scale of lane (., g) on either side covers K-block g; output lane L
+// register r = row 4(L/16) + r, column L % 16. All 16 rows of A hold the same
+// token, so every output row carries that token's result.
+//
+// Work: a work-group is (slot, 16 rows of the gate and of the up matrix). Its four
+// waves take contiguous quarters of K (in 128-wide steps) and issue all their
+// weight loads before anything else; their partial sums meet in LDS and are added
+// in wave order.
+#include <hip/hip_ext.h>
+
+#include "moeq_device.h"
+#include "moeq_kernels.h"
+
+namespace moeq {
+
+namespace {
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int MX_WAVES = 4;
+constexpr int MX_STEPS = 8;                           // K steps of 128 per wave
+constexpr int MX_KMAX = 128 * MX_WAVES * MX_STEPS;    // 4096
+
+// e8m0 exponent of a 32-block with maximum a: the smallest 2^e with a / 2^e <= 448
+// (e = p - 9 if the frexp mantissa of a is <= 0.875, else p - 8), clamped to the
+// code range; zero or subnormal maxima give 0.
+__device__ __forceinline__ uint32_t gu_mx_exponent(float amax) {
+  const uint32_t ab = f2u(amax);
+  if (ab < 0x00800000u) return 0u;
+  const int p = (int)(ab >> 23) - 126;
+  const uint32_t frac = ab & 0x007FFFFFu;
+  const int e = (frac <= 0x00600000u) ? p - 9 : p - 8;
+  const int E = e + 127;
+  return (uint32_t)(E < 0 ? 0 : (E > 254 ? 254 : E));
+}
+
+struct MxStage {
+  uint8_t code[2][MX_KMAX];  // E4M3 codes of hi and lo
+  uint8_t sc[2][MX_KMAX / 32];
+};
+
+__global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
+  __shared__ MxStage st;
+  __shared__ float red[MX_WAVES][2][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.y;
+  const int n0 = blockIdx.x * 16;
+  const int K = P.cols;
+  const int nsteps = K / 128;
+  const int e = P.ids[slot];
+  const bool ok = e >= 0 && e < P.n_experts;
+
+  // The token's values first (the conversion below waits only for them), then every
+  // weight load of the wave; steps past the wave's last re-read it and are not used. Thread t converts values 16t .. 16t + 15 (two
+  // threads per 32-block; K <= 4096 = 16 x 256); threads past K re-read the last 16.
+  const int k0 = min(16 * (int)threadIdx.x, K - 16);
+  const uint16_t* xr = reinterpret_cast<const uint16_t*>(P.act) + k0;
+  const u32x4 v0 = ld16(xr), v1 = ld16(xr + 8);
+  __builtin_amdgcn_sched_barrier(0);
+  const int n = lane & 15, g = lane >> 4;
+  const int rn = min(n0 + n, P.rows - 1);
+  const int ec = ok ? e : 0;
+  const uint8_t* wd[2];
+  const uint8_t* ws[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    wd[mt] = P.w[mt].data + (size_t)ec * P.w[mt].estride + (size_t)rn * (K / 2);
+    ws[mt] = P.w[mt].scales + (size_t)ec * P.w[mt].sestride + (size_t)rn * (K / 32);
+  }
+  // Wave w takes the contiguous K steps [w spw, (w + 1) spw): consecutive steps of
+  // one wave complete each other's 128-byte lines.
+  const int spw = 4 * ((nsteps + 4 * MX_WAVES - 1) / (4 * MX_WAVES));  // a multiple of 4 (aligned scale runs)
+  const int s0 = wave * spw;
+  const int my_steps = max(0, min(spw, nsteps - s0));  // uniform per wave
+  u32x4 q[2][MX_STEPS];
+  u32x4 sbv4[2][MX_STEPS / 4];  // chunk scales 4 s0 .. 4 s0 + 31 of row rn: dword i = step s0 + i
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+#pragma unroll
+    for (int j = 0; j < MX_STEPS / 4; j++)
+      sbv4[mt][j] = ld16(ws[mt] + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
+  }
+#pragma unroll
+  for (int i = 0; i < MX_STEPS; i++) {
+    const int s = min(s0 + min(i, max(my_steps - 1, 0)), nsteps - 1);
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) q[mt][i] = ld16(wd[mt] + (size_t)s * 64 + 16 * g);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // x -> hi/lo E4M3 codes and per-32 scales in LDS.
+  if (16 * (int)threadIdx.x < K) {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      x[2 * j] = u2f(v0[j] << 16);
+      x[2 * j + 1] = u2f(v0[j] & 0xFFFF0000u);
+      x[8 + 2 * j] = u2f(v1[j] << 16);
+      x[8 + 2 * j + 1] = u2f(v1[j] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int term = 0; term < 2; term++) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));  // the block's other half
+      const uint32_t E = gu_mx_exponent(amax);
+      const int sh = 127 - (int)E;  // x / 2^(E - 127) is at most 448: no clipping
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+            i16x2_t{0, 0}, __builtin_ldexpf(x[4 * j], sh), __builtin_ldexpf(x[4 * j + 1], sh), 1.0f, false);
+        const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+            lo, __builtin_ldexpf(x[4 * j + 2], sh), __builtin_ldexpf(x[4 * j + 3], sh), 1.0f, true);
+        w[j] = (amax == 0.f) ? 0u : __builtin_bit_cast(uint32_t, hi);
+      }
+      *reinterpret_cast<u32x4*>(&st.code[term][k0]) = u32x4{w[0], w[1], w[2], w[3]};
+      if ((threadIdx.x & 1) == 0) st.sc[term][k0 / 32] = (uint8_t)E;
+      if (term == 0) {
+        // residual x - hi, exact in fp32
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, false);
+          const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, true);
+          x[4 * j] -= __builtin_ldexpf(a[0], -sh);
+          x[4 * j + 1] -= __builtin_ldexpf(a[1], -sh);
+          x[4 * j + 2] -= __builtin_ldexpf(b[0], -sh);
+          x[4 * j + 3] -= __builtin_ldexpf(b[1], -sh);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < MX_STEPS; i++) {
+    if (i < my_steps) {
+      const int s = s0 + i;
+#pragma unroll
+      for (int term = 0; term < 2; term++) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(&st.code[term][128 * s + 16 * g]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(&st.code[term][128 * s + 64 + 16 * g]);
+        const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const int sa = st.sc[term][4 * s + g];
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+          // only the low four registers of an FP4 operand are read
+          const i32x8_t bv =
+              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
+          const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));  // this lane's chunk scale, low byte
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
+        }
+      }
+    }
+  }
+  // Prefetches past the wave's last step are never used: let them land first.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane < 16) {
+    red[wave][0][lane] = acc[0][0];
+    red[wave][1][lane] = acc[1][0];
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float gs = 0.f, us = 0.f;
+#pragma unroll
+    for (int w = 0; w < MX_WAVES; w++) {
+      gs += red[w][0][threadIdx.x];
+      us += red[w][1][threadIdx.x];
+    }
+    const int r = n0 + (int)threadIdx.x;
+    if (r < P.rows) P.out[(size_t)slot * P.rows + r] = ok ? silu_mul(gs, us) : 0.f;
+    if (!ok && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(P.err, 1u);
+  }
+}
+
+}  // namespace
+
+// K a multiple of 512: every wave's 16-byte runs of chunk scales stay inside the row.
+bool gu1_mx4_fits(int rows, int cols) { return rows > 0 && cols > 0 && cols % 512 == 0 && cols <= MX_KMAX; }
+
+hipError_t launch_gu1_mx4(const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev) {
+  if (!gu1_mx4_fits(p.rows, p.cols)) return hipErrorInvalidValue;
+  dim3 g((unsigned)((p.rows + 15) / 16), (unsigned)n_slots), b(64 * MX_WAVES);
+  if (ev) hipExtLaunchKernelGGL(k_gu1_mx4, g, b, 0, s, ev->start, ev->stop, 0, p);
+  else hipLaunchKernelGGL(k_gu1_mx4, g, b, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moeq

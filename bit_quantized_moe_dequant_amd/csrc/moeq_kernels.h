@@ -131,6 +131,9 @@ hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s);
 bool fused1_supported(int fg, int fd, int hidden, int inter, int top_k);
 hipError_t launch_fused1(int fg, int fd, const FusedParams& p, hipStream_t s);
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int n_slots, hipStream_t s);
+bool gu1_mx4_fits(int rows, int cols);  // cols % 512 == 0, cols <= 4096
+// Single-token gate/up + SwiGLU for MXFP4 on the block-scaled matrix instruction.
+hipError_t launch_gu1_mx4(const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev);
 bool gu_iq2_fits(int rows, int cols);  // cols % 256 == 0
 // Grouped gate/up + SwiGLU for IQ2_XXS on the bf16 matrix instruction (T > 1).
 hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, hipStream_t s);

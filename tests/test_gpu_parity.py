@@ -186,6 +186,8 @@ SMALL = [
     (3, 4, 512, 768, 4, 2),
     (5, 5, 512, 256, 4, 2),
     (2, 2, 640, 384, 4, 4),
+    (1, 1, 1536, 256, 4, 2),    # bs=1 MXFP4 gate/up on the matrix unit: the fourth wave gets no K step
+    (1, 1, 512, 128, 3, 2),     # ... and a single wave of K steps
 ]
 
 
@@ -240,6 +242,29 @@ def test_iq2_grouped_gate_up(T, I):
     ok = np.ones((T, 2), bool)
     ok[1, 0] = False
     assert rel_err(h[ok], ref_h[ok]) < TOL
+
+
+def test_mxfp4_gate_up_scale_alignment():
+    """Single-token MXFP4 gate/up reads its chunk scales 16 bytes at a time on the
+    matrix-instruction path; scale planes only 4-byte aligned (the minimum the ABI
+    asks for) take the GEMV path instead. Both must match the oracle."""
+    say("mxfp4 scale alignment")
+    spec = workloads.LayerSpec(1024, 512, 8, 3, mq.FMT_MXFP4, mq.FMT_MXFP4, seed=4501)
+    layer = upload_layer(spec)
+    ids, rw = synth.uniform_routing(spec.seed, 1, 8, 3)
+    x = synth.activations_bf16(spec.seed + 1, 1, 1024)
+    ref, ref_h = moe.moe_layer(x, ids, rw, oracle_weight_fn(spec))
+    y16 = mq.expert_forward(layer, x_tensor(x), cuda(ids), cuda(rw)).cpu().numpy()
+    for w in (layer.gate, layer.up):
+        buf = torch.empty(w.scales.numel() + 4, dtype=torch.uint8, device="cuda")
+        buf[4:].copy_(w.scales)
+        w.scales = buf[4:]
+        assert w.scales.data_ptr() % 16 == 4
+    h4 = mq.gate_up(layer, x_tensor(x), cuda(ids)).cpu().numpy()
+    y4 = mq.expert_forward(layer, x_tensor(x), cuda(ids), cuda(rw)).cpu().numpy()
+    assert rel_err(y16, ref) < TOL
+    assert rel_err(y4, ref) < TOL
+    assert rel_err(h4.reshape(1, 3, 512), ref_h) < TOL
 
 
 def test_one_launch_layer_repeats_exactly():
