@@ -508,6 +508,11 @@ static hipError_t down1_f(const Down1Params& p, int cpl, dim3 g, dim3 b, hipStre
 }
 
 hipError_t launch_down1(int fmt, const Down1Params& p, hipStream_t s) {
+  // MXFP4: straight into the matrix unit (16-byte scale runs and h loads need
+  // 16-byte aligned scale planes and h).
+  if (fmt == FMT_MXFP4 && down1_mx4_fits(p.rows, p.cols, p.top_k) && (uintptr_t)p.w.scales % 16 == 0 &&
+      p.w.sestride % 16 == 0 && (uintptr_t)p.h % 16 == 0)
+    return launch_down1_mx4(p, s);
   int lpr, cpl;
   if (!chunk_geometry(fmt, p.cols, &lpr, &cpl)) return hipErrorInvalidValue;
   Down1Params q = p;

@@ -198,10 +198,160 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
   }
 }
 
+// ---------------------------------------------------------------- down, one token
+// The same instruction for the down projection of one token: y = sum over the
+// routed slots k of w_k D_{e_k} h_k (a route-weighted sum of the routed experts'
+// outputs). h is fp32, so it is split into three E4M3 terms (about 12 significant
+// bits; each residual is exact in fp32, and the bits dropped lie below 2^-13 of the
+// block maximum, well inside the projection tolerance). A work-group takes 16
+// output rows for all slots: two waves per slot, each half of K; the partials are
+// combined in LDS in slot order with the route weights.
+constexpr int DM_TERMS = 3;
+constexpr int DM_KPARTS = 2;
+constexpr int DM_KMAX = 128 * DM_KPARTS * MX_STEPS;  // 2048
+constexpr int DM_SLOTS = 8;
+
+struct DmStage {
+  uint8_t code[DM_TERMS][DM_SLOTS * DM_KMAX];
+  uint8_t sc[DM_TERMS][DM_SLOTS * DM_KMAX / 32];
+};
+
+__global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Params P) {
+  __shared__ DmStage st;
+  __shared__ float red[DM_SLOTS * DM_KPARTS][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = wave / DM_KPARTS, part = wave % DM_KPARTS;
+  const int n0 = blockIdx.x * 16;
+  const int K = P.cols;
+  const int nsteps = K / 128;
+  const int e = P.ids[slot];
+  const bool ok = e >= 0 && e < P.n_experts;
+
+  // h first (the conversion waits only for it): thread t converts values 16t ..
+  // 16t + 15 of the slots' concatenated h, [top_k][K] (two threads per 32-block;
+  // the block size is 64 x 2 x top_k threads = top_k x K / 16 for K = 2048).
+  const int total = P.top_k * K;
+  const int v0i = min(16 * (int)threadIdx.x, total - 16);
+  const float* hp = P.h + v0i;
+  const u32x4 hv0 = ld16(hp), hv1 = ld16(hp + 4), hv2 = ld16(hp + 8), hv3 = ld16(hp + 12);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Weights: K steps [part spw, (part + 1) spw) of row n0 + n of expert e.
+  const int n = lane & 15, g = lane >> 4;
+  const int rn = min(n0 + n, P.rows - 1);
+  const int ec = ok ? e : 0;
+  const uint8_t* wd = P.w.data + (size_t)ec * P.w.estride + (size_t)rn * (K / 2);
+  const uint8_t* ws = P.w.scales + (size_t)ec * P.w.sestride + (size_t)rn * (K / 32);
+  const int spw = 4 * ((nsteps + 4 * DM_KPARTS - 1) / (4 * DM_KPARTS));  // a multiple of 4 (aligned scale runs)
+  const int s0 = part * spw;
+  const int my_steps = max(0, min(spw, nsteps - s0));
+  u32x4 sbv4[MX_STEPS / 4];
+#pragma unroll
+  for (int j = 0; j < MX_STEPS / 4; j++) sbv4[j] = ld16(ws + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
+  u32x4 q[MX_STEPS];
+#pragma unroll
+  for (int i = 0; i < MX_STEPS; i++)
+    q[i] = ld16(wd + (size_t)min(s0 + min(i, max(my_steps - 1, 0)), nsteps - 1) * 64 + 16 * g);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // h -> three E4M3 terms with per-32 scales in LDS (one pass: K <= 2048).
+  if (16 * (int)threadIdx.x < total) {
+    const int v = v0i;
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      x[j] = u2f(hv0[j]);
+      x[4 + j] = u2f(hv1[j]);
+      x[8 + j] = u2f(hv2[j]);
+      x[12 + j] = u2f(hv3[j]);
+    }
+#pragma unroll
+    for (int term = 0; term < DM_TERMS; term++) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));  // the block's other half
+      const uint32_t E = gu_mx_exponent(amax);
+      const int sh = 127 - (int)E;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+            i16x2_t{0, 0}, __builtin_ldexpf(x[4 * j], sh), __builtin_ldexpf(x[4 * j + 1], sh), 1.0f, false);
+        const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+            lo, __builtin_ldexpf(x[4 * j + 2], sh), __builtin_ldexpf(x[4 * j + 3], sh), 1.0f, true);
+        w[j] = (amax == 0.f) ? 0u : __builtin_bit_cast(uint32_t, hi);
+      }
+      *reinterpret_cast<u32x4*>(&st.code[term][v]) = u32x4{w[0], w[1], w[2], w[3]};
+      if ((threadIdx.x & 1) == 0) st.sc[term][v / 32] = (uint8_t)E;
+      if (term + 1 < DM_TERMS) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {  // residual, exact in fp32
+          const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, false);
+          const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, true);
+          x[4 * j] -= __builtin_ldexpf(a[0], -sh);
+          x[4 * j + 1] -= __builtin_ldexpf(a[1], -sh);
+          x[4 * j + 2] -= __builtin_ldexpf(b[0], -sh);
+          x[4 * j + 3] -= __builtin_ldexpf(b[1], -sh);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int hb = slot * K;  // this slot's h among the staged codes
+#pragma unroll
+  for (int i = 0; i < MX_STEPS; i++) {
+    if (i < my_steps) {
+      const int s = s0 + i;
+      const i32x8_t bv = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[i], q[i], 0, 1, 2, 3, -1, -1, -1, -1));
+      const int sbv = (int)(sbv4[i >> 2][i & 3] >> (8 * g));
+#pragma unroll
+      for (int term = 0; term < DM_TERMS; term++) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(&st.code[term][hb + 128 * s + 16 * g]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(&st.code[term][hb + 128 * s + 64 + 16 * g]);
+        const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const int sa = st.sc[term][(hb + 128 * s) / 32 + g];
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sbv);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // unused prefetches land before the end
+  if (lane < 16) red[wave][lane] = ok ? acc[0] : 0.f;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float y = 0.f;
+    for (int k = 0; k < P.top_k; k++) {
+      float pk = 0.f;
+#pragma unroll
+      for (int h = 0; h < DM_KPARTS; h++) pk += red[k * DM_KPARTS + h][threadIdx.x];
+      y += pk * P.rw[k];
+    }
+    const int r = n0 + (int)threadIdx.x;
+    if (r < P.rows) P.y[r] = y;
+  }
+  if (!ok && blockIdx.x == 0 && lane == 0 && part == 0) atomicOr(P.err, 1u);
+}
+
 }  // namespace
 
 // K a multiple of 512: every wave's 16-byte runs of chunk scales stay inside the row.
 bool gu1_mx4_fits(int rows, int cols) { return rows > 0 && cols > 0 && cols % 512 == 0 && cols <= MX_KMAX; }
+
+// K a multiple of 512 up to 2048, at most 8 slots.
+bool down1_mx4_fits(int rows, int cols, int top_k) {
+  return rows > 0 && cols > 0 && cols % 512 == 0 && cols <= DM_KMAX && top_k >= 1 && top_k <= DM_SLOTS;
+}
+
+hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s) {
+  if (!down1_mx4_fits(p.rows, p.cols, p.top_k)) return hipErrorInvalidValue;
+  dim3 g((unsigned)((p.rows + 15) / 16)), b((unsigned)(64 * DM_KPARTS * p.top_k));
+  hipLaunchKernelGGL(k_down1_mx4, g, b, 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_gu1_mx4(const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev) {
   if (!gu1_mx4_fits(p.rows, p.cols)) return hipErrorInvalidValue;

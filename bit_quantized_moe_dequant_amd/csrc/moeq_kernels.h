@@ -134,6 +134,9 @@ hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int n_slots, hip
 bool gu1_mx4_fits(int rows, int cols);  // cols % 512 == 0, cols <= 4096
 // Single-token gate/up + SwiGLU for MXFP4 on the block-scaled matrix instruction.
 hipError_t launch_gu1_mx4(const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev);
+bool down1_mx4_fits(int rows, int cols, int top_k);  // cols % 512 == 0, cols <= 2048, top_k <= 8
+// Single-token down + weighted combine for MXFP4 on the block-scaled matrix instruction.
+hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s);
 bool gu_iq2_fits(int rows, int cols);  // cols % 256 == 0
 // Grouped gate/up + SwiGLU for IQ2_XXS on the bf16 matrix instruction (T > 1).
 hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, hipStream_t s);

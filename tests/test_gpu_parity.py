@@ -188,6 +188,8 @@ SMALL = [
     (2, 2, 640, 384, 4, 4),
     (1, 1, 1536, 256, 4, 2),    # bs=1 MXFP4 gate/up on the matrix unit: the fourth wave gets no K step
     (1, 1, 512, 128, 3, 2),     # ... and a single wave of K steps
+    (1, 1, 1024, 512, 16, 8),   # bs=1 MXFP4 down on the matrix unit with its largest work-group (8 slots)
+    (1, 1, 1024, 512, 16, 10),  # more slots than it takes: the GEMV path
 ]
 
 
@@ -319,6 +321,29 @@ def test_out_of_range_expert_ids(T):
     bad = (ids < 0) | (ids >= 8)
     rw2[bad] = 0
     ids2[bad] = 0
+    ref, _ = moe.moe_layer(x, ids2, rw2, oracle_weight_fn(spec))
+    assert rel_err(y, ref) < TOL
+
+
+def test_out_of_range_expert_ids_matrix_path():
+    """bs=1 with MXFP4 gate/up and down both on the block-scaled matrix instruction
+    (K a multiple of 512): an out-of-range id contributes nothing and sets the
+    error bit."""
+    say("bad ids, matrix path")
+    spec = workloads.LayerSpec(1024, 512, 8, 3, 1, 1, seed=77)
+    layer = upload_layer(spec)
+    ids, rw = synth.uniform_routing(8, 1, 8, 3)
+    ids = ids.copy()
+    ids[0, 1] = 300
+    x = synth.activations_bf16(9, 1, 1024)
+    ws = layer.workspace(1)
+    mq.check_device_error(ws)
+    y = mq.expert_forward(layer, x_tensor(x), cuda(ids), cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    rw2 = rw.copy()
+    ids2 = ids.copy()
+    rw2[0, 1] = 0
+    ids2[0, 1] = 0
     ref, _ = moe.moe_layer(x, ids2, rw2, oracle_weight_fn(spec))
     assert rel_err(y, ref) < TOL
 
