@@ -203,7 +203,7 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
   if (L->gate.fmt == MOEQ_FMT_IQ2_XXS && gu_iq2_fits(L->inter, L->hidden))
-    return hip_rc(launch_gu_iq2(p, slots, s));
+    return hip_rc(launch_gu_iq2(p, slots, (double)T * L->top_k >= 8.0 * L->n_experts, s));
   return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, grouped_wide(L, T) ? 4 : 1, s, ev));
 }
 

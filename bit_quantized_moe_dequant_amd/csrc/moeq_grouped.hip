@@ -191,6 +191,153 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
+// ---------------------------------------------------------------- many tokens per expert
+// Prefill-sized batches: each superblock is decoded once (bf16 words and sub-block
+// scales kept in registers) and applied to GW_NT 16-token tiles per pass, so the
+// decode is shared by up to 16 GW_NT tokens instead of 16. The weights stream
+// through two buffers as above; a pass loads its tiles' activations per
+// superblock, before the decode, so the decode covers their latency.
+constexpr int GW_NT = 2;
+
+struct GwBuf {
+  u32x4 w[2][4];
+  uint32_t d[2];
+};
+
+__device__ __forceinline__ void gw_issue(const GiStreams& st, int sb, GwBuf& b) {
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      b.w[mt][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.w[mt], st.w_off + 16 * i, sb * 64, 0));
+    b.d[mt] = __builtin_amdgcn_raw_buffer_load_b16(st.s[mt], st.s_off, sb * 2, 0);
+  }
+}
+
+// One superblock: activations of the pass's tiles, decode, then the multiplies.
+__device__ __forceinline__ void gw_compute(const GiStreams& st, const int (&x_off)[GW_NT], int nt, int sb,
+                                           const GwBuf& b, int g, const Iq2Lds* t, const GiSigns* sg,
+                                           f32x4_t (&acc)[GW_NT][2]) {
+  u32x4 xv[GW_NT][8];
+#pragma unroll
+  for (int ti = 0; ti < GW_NT; ti++)
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      xv[ti][j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, x_off[ti] + 64 * j, sb * 512, 0));
+  u32x4 wv[2][8];
+  float db[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    const float d8 = half_bits_f32(b.d[mt]) * 0.125f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t a0 = b.w[mt][j >> 1][2 * (j & 1)], a1 = b.w[mt][j >> 1][2 * (j & 1) + 1];
+      const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
+      const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
+      const u32x4 m = sg->w[code];
+      wv[mt][j] = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
+      db[mt][j] = d8 * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
+    }
+  }
+#pragma unroll
+  for (int ti = 0; ti < GW_NT; ti++) {
+    if (ti < nt) {
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[ti][j]),
+                                                                    __builtin_bit_cast(bf16x8_t, wv[mt][j]),
+                                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; r++) acc[ti][mt][r] = __builtin_fmaf(c[r], db[mt][j], acc[ti][mt][r]);
+        }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_gu_iq2_wide(GemvParams P) {
+  __shared__ Iq2Lds lds_tab[1];
+  __shared__ GiSigns signs[1];
+  iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
+  if (threadIdx.x < 128) {
+    uint32_t m[4];
+    iq2_sign_words(threadIdx.x, m);
+    signs[0].w[threadIdx.x] = u32x4{m[0], m[1], m[2], m[3]};
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int slot = blockIdx.y;
+  if (slot >= P.route.n_slots()[0]) return;
+  const int e = P.route.slots()[slot];
+  const int pstart = P.route.offsets()[e];
+  const int M = P.route.offsets()[e + 1] - pstart;
+  const int n0 = blockIdx.x * GI_ROWS + wave * 16;
+  if (n0 >= P.rows || M <= 0) return;
+  if (e < 0 || e >= P.n_experts) {
+    for (int m = 0; m < M; m++) {
+      const int pair = P.route.perm()[pstart + m];
+      if (lane < 16 && n0 + lane < P.rows) P.out[(size_t)pair * P.rows + n0 + lane] = 0.f;
+    }
+    return;
+  }
+
+  const int nsb = P.cols / 256;
+  const int rn = min(n0 + n, P.rows - 1);
+  GiStreams st;
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    st.w[mt] = gi_buffer(P.w[mt].data + (size_t)e * P.w[mt].estride);
+    st.s[mt] = gi_buffer(P.w[mt].scales + (size_t)e * P.w[mt].sestride);
+  }
+  st.x = gi_buffer(P.act);
+  st.w_off = rn * nsb * 64;
+  st.s_off = rn * nsb * 2;
+
+  for (int m0 = 0; m0 < M; m0 += 16 * GW_NT) {
+    const int nt = min(GW_NT, (M - m0 + 15) / 16);  // uniform
+    int x_off[GW_NT];
+#pragma unroll
+    for (int ti = 0; ti < GW_NT; ti++) {
+      const int pa = P.route.perm()[pstart + min(m0 + 16 * ti + n, M - 1)];
+      x_off[ti] = (pa / P.top_k) * P.cols * 2 + 16 * g;
+    }
+    f32x4_t acc[GW_NT][2];
+#pragma unroll
+    for (int ti = 0; ti < GW_NT; ti++) acc[ti][0] = acc[ti][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    GwBuf A, B;
+    gw_issue(st, 0, A);
+    for (int sb = 0;; sb += 2) {
+      gw_issue(st, min(sb + 1, nsb - 1), B);
+      __builtin_amdgcn_sched_barrier(0);
+      gw_compute(st, x_off, nt, sb, A, g, &lds_tab[0], &signs[0], acc);
+      if (sb + 1 >= nsb) break;
+      gw_issue(st, min(sb + 2, nsb - 1), A);
+      __builtin_amdgcn_sched_barrier(0);
+      gw_compute(st, x_off, nt, sb + 1, B, g, &lds_tab[0], &signs[0], acc);
+      if (sb + 2 >= nsb) break;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (n0 + n < P.rows) {
+#pragma unroll
+      for (int ti = 0; ti < GW_NT; ti++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int m = m0 + 16 * ti + 4 * g + r;
+          if (ti < nt && m < M) {
+            const int pair = P.route.perm()[pstart + m];
+            P.out[(size_t)pair * P.rows + n0 + n] = silu_mul(acc[ti][0][r], acc[ti][1][r]);
+          }
+        }
+    }
+  }
+}
+
 }  // namespace
 
 // Buffer offsets are 32-bit: an expert's data plane and the activations must stay
@@ -199,10 +346,11 @@ bool gu_iq2_fits(int rows, int cols) {
   return rows > 0 && cols > 0 && cols % 256 == 0 && (long)rows * (cols / 256) * 64 < (1L << 31);
 }
 
-hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, hipStream_t s) {
+hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, bool wide, hipStream_t s) {
   if (!gu_iq2_fits(p.rows, p.cols) || (long)p.T * p.cols * 2 >= (1L << 31)) return hipErrorInvalidValue;
   dim3 g((unsigned)((p.rows + GI_ROWS - 1) / GI_ROWS), (unsigned)n_slots);
-  hipLaunchKernelGGL(k_gu_iq2, g, dim3(64 * GI_WAVES), 0, s, p);
+  if (wide) hipLaunchKernelGGL(k_gu_iq2_wide, g, dim3(64 * GI_WAVES), 0, s, p);
+  else hipLaunchKernelGGL(k_gu_iq2, g, dim3(64 * GI_WAVES), 0, s, p);
   return hipGetLastError();
 }
 

@@ -139,7 +139,8 @@ bool down1_mx4_fits(int rows, int cols, int top_k);  // cols % 512 == 0, cols <=
 hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s);
 bool gu_iq2_fits(int rows, int cols);  // cols % 256 == 0
 // Grouped gate/up + SwiGLU for IQ2_XXS on the bf16 matrix instruction (T > 1).
-hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, hipStream_t s);
+// wide: decode each superblock once for two 16-token tiles (many tokens per expert).
+hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, bool wide, hipStream_t s);
 bool linear_fp8_fits(int rows, int cols);  // rows % 128 == 0, cols % 256 == 0
 hipError_t launch_linear_fp8(const LinearParams& p, hipStream_t s);
 
