@@ -18,8 +18,13 @@
 // row) with K = 32(L/16) + [0, 32), low nibble first; A lane L = row L % 16 with
 // bytes 0-15 at K = 16(L/16) + [0, 16) and bytes 16-31 at K = 64 + 16(L/16) +
 // [0, 16); the scale of lane (., g) on either side covers K-block g; output lane L
-// register r = row 4(L/16) + r, column L % 16. All 16 rows of A hold the same
-// token, so every output row carries that token's result.
+// register r = row 4(L/16) + r, column L % 16. With one token, the rows of A carry
+// the terms of its split instead of tokens: row t holds term t with that term's
+// scales, the rows past the last term are zero (scale code 0), and the token's
+// result is the sum of output rows 0 .. terms-1 (lanes 0-15, registers 0 .. terms-1).
+// One instruction thus multiplies every term by the weights; with a term per
+// instruction the matrix unit's work (about 44 clocks per 16 x 128 weights on a
+// SIMD) was a large share of the weight stream's time and did not all hide under it.
 //
 // Work: a work-group is (slot, 16 rows of the gate and of the up matrix). Its four
 // waves take contiguous quarters of K (in 128-wide steps) and issue all their
@@ -41,6 +46,14 @@ typedef short i16x2_t __attribute__((ext_vector_type(2)));
 constexpr int MX_WAVES = 4;
 constexpr int MX_STEPS = 8;                           // K steps of 128 per wave
 constexpr int MX_KMAX = 128 * MX_WAVES * MX_STEPS;    // 4096
+#ifndef MOEQ_MX_DEPTH
+#define MOEQ_MX_DEPTH 8
+#endif
+#ifndef MOEQ_DM_DEPTH
+#define MOEQ_DM_DEPTH 8
+#endif
+constexpr int MX_DEPTH = MOEQ_MX_DEPTH;  // gate/up K steps in flight per wave
+constexpr int DM_DEPTH = MOEQ_DM_DEPTH;  // down K steps in flight per wave
 
 // e8m0 exponent of a 32-block with maximum a: the smallest 2^e with a / 2^e <= 448
 // (e = p - 9 if the frexp mantissa of a is <= 0.875, else p - 8), clamped to the
@@ -103,12 +116,14 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
     for (int j = 0; j < MX_STEPS / 4; j++)
       sbv4[mt][j] = ld16(ws[mt] + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
   }
-#pragma unroll
-  for (int i = 0; i < MX_STEPS; i++) {
+  // Step i's chunk of row rn (steps past the wave's last re-read that one).
+  auto load_step = [&](int i) {
     const int s = min(s0 + min(i, max(my_steps - 1, 0)), nsteps - 1);
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) q[mt][i] = ld16(wd[mt] + (size_t)s * 64 + 16 * g);
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < MX_DEPTH; i++) load_step(i);
   __builtin_amdgcn_sched_barrier(0);
 
   // x -> hi/lo E4M3 codes and per-32 scales in LDS.
@@ -159,30 +174,34 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int i = 0; i < MX_STEPS; i++) {
+    if (i + MX_DEPTH < MX_STEPS) load_step(i + MX_DEPTH);  // keep MX_DEPTH steps in flight
+    __builtin_amdgcn_sched_barrier(0);
     if (i < my_steps) {
       const int s = s0 + i;
+      // A row n < 2 is term n of x (hi, lo); rows 2-15 are zero with scale code 0.
+      u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
+      int sa = 0;
+      if (n < 2) {
+        a0 = *reinterpret_cast<const u32x4*>(&st.code[n][128 * s + 16 * g]);
+        a1 = *reinterpret_cast<const u32x4*>(&st.code[n][128 * s + 64 + 16 * g]);
+        sa = st.sc[n][4 * s + g];
+      }
+      const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int term = 0; term < 2; term++) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(&st.code[term][128 * s + 16 * g]);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(&st.code[term][128 * s + 64 + 16 * g]);
-        const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const int sa = st.sc[term][4 * s + g];
-#pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
-          // only the low four registers of an FP4 operand are read
-          const i32x8_t bv =
-              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
-          const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));  // this lane's chunk scale, low byte
-          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
-        }
+      for (int mt = 0; mt < 2; mt++) {
+        // only the low four registers of an FP4 operand are read
+        const i32x8_t bv =
+            __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
+        const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));  // this lane's chunk scale, low byte
+        acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
       }
     }
   }
   // Prefetches past the wave's last step are never used: let them land first.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (lane < 16) {
-    red[wave][0][lane] = acc[0][0];
-    red[wave][1][lane] = acc[1][0];
+  if (lane < 16) {  // output rows 0 and 1: the hi and lo products
+    red[wave][0][lane] = acc[0][0] + acc[0][1];
+    red[wave][1][lane] = acc[1][0] + acc[1][1];
   }
   __syncthreads();
   if (threadIdx.x < 16) {
@@ -235,6 +254,9 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
   const int total = P.top_k * K;
   const int v0i = min(16 * (int)threadIdx.x, total - 16);
   const float* hp = P.h + v0i;
+  // Route weights before anything else: lane k holds rw[k] for the combine at the
+  // end, which would otherwise wait a memory round trip after the last barrier.
+  const float rwv = P.rw[min(lane, P.top_k - 1)];
   const u32x4 hv0 = ld16(hp), hv1 = ld16(hp + 4), hv2 = ld16(hp + 8), hv3 = ld16(hp + 12);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -251,9 +273,9 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
 #pragma unroll
   for (int j = 0; j < MX_STEPS / 4; j++) sbv4[j] = ld16(ws + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
   u32x4 q[MX_STEPS];
+  auto load_step = [&](int i) { q[i] = ld16(wd + (size_t)min(s0 + min(i, max(my_steps - 1, 0)), nsteps - 1) * 64 + 16 * g); };
 #pragma unroll
-  for (int i = 0; i < MX_STEPS; i++)
-    q[i] = ld16(wd + (size_t)min(s0 + min(i, max(my_steps - 1, 0)), nsteps - 1) * 64 + 16 * g);
+  for (int i = 0; i < DM_DEPTH; i++) load_step(i);
   __builtin_amdgcn_sched_barrier(0);
 
   // h -> three E4M3 terms with per-32 scales in LDS (one pass: K <= 2048).
@@ -305,22 +327,27 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
   const int hb = slot * K;  // this slot's h among the staged codes
 #pragma unroll
   for (int i = 0; i < MX_STEPS; i++) {
+    if (i + DM_DEPTH < MX_STEPS) load_step(i + DM_DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
     if (i < my_steps) {
       const int s = s0 + i;
       const i32x8_t bv = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[i], q[i], 0, 1, 2, 3, -1, -1, -1, -1));
       const int sbv = (int)(sbv4[i >> 2][i & 3] >> (8 * g));
-#pragma unroll
-      for (int term = 0; term < DM_TERMS; term++) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(&st.code[term][hb + 128 * s + 16 * g]);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(&st.code[term][hb + 128 * s + 64 + 16 * g]);
-        const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const int sa = st.sc[term][(hb + 128 * s) / 32 + g];
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sbv);
+      // A row n < DM_TERMS is term n of h; the other rows are zero with scale code 0.
+      u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
+      int sa = 0;
+      if (n < DM_TERMS) {
+        a0 = *reinterpret_cast<const u32x4*>(&st.code[n][hb + 128 * s + 16 * g]);
+        a1 = *reinterpret_cast<const u32x4*>(&st.code[n][hb + 128 * s + 64 + 16 * g]);
+        sa = st.sc[n][(hb + 128 * s) / 32 + g];
       }
+      const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sbv);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // unused prefetches land before the end
-  if (lane < 16) red[wave][lane] = ok ? acc[0] : 0.f;
+  static_assert(DM_TERMS == 3, "output rows 0-2 hold the terms' products");
+  if (lane < 16) red[wave][lane] = ok ? acc[0] + acc[1] + acc[2] : 0.f;
   __syncthreads();
   if (threadIdx.x < 16) {
     float y = 0.f;
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
       float pk = 0.f;
 #pragma unroll
       for (int h = 0; h < DM_KPARTS; h++) pk += red[k * DM_KPARTS + h][threadIdx.x];
-      y += pk * P.rw[k];
+      y += pk * u2f(__builtin_amdgcn_readlane(f2u(rwv), k));
     }
     const int r = n0 + (int)threadIdx.x;
     if (r < P.rows) P.y[r] = y;
