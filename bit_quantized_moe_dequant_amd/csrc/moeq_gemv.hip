@@ -464,13 +464,14 @@ static hipError_t gemv_f(int epi, const GemvParams& p, int cpl, dim3 g, int mt, 
 
 hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int mt, hipStream_t s,
                        const LaunchEvents* ev) {
-  // One token, MXFP4: the weights go straight into the matrix unit (its scale runs
-  // are read 16 bytes at a time, so the scale planes must be 16-byte aligned).
+  // One token, MXFP4 or NVFP4: the weights go straight into the matrix unit (its
+  // scale runs are read 16 bytes at a time, so the scale planes must be 16-byte
+  // aligned).
   const bool sc16 = ((uintptr_t)p.w[0].scales % 16 == 0) && ((uintptr_t)p.w[1].scales % 16 == 0) &&
                     p.w[0].sestride % 16 == 0 && p.w[1].sestride % 16 == 0;
-  if (fmt == FMT_MXFP4 && epi == EPI_SWIGLU && p.mode == MODE_DIRECT && mt == 1 && sc16 &&
+  if ((fmt == FMT_MXFP4 || fmt == FMT_NVFP4) && epi == EPI_SWIGLU && p.mode == MODE_DIRECT && mt == 1 && sc16 &&
       gu1_mx4_fits(p.rows, p.cols))
-    return launch_gu1_mx4(p, n_slots, s, ev);
+    return launch_gu1_fp4(fmt, p, n_slots, s, ev);
   int lpr, cpl;
   if (!chunk_geometry(fmt, p.cols, &lpr, &cpl)) return hipErrorInvalidValue;
   GemvParams q = p;

@@ -1,5 +1,6 @@
-// Single-token gate/up + SwiGLU for MXFP4 experts on the block-scaled matrix
-// instruction v_mfma_scale_f32_16x16x128_f8f6f4, with no weight decode on the VALU.
+// Single-token gate/up + SwiGLU for MXFP4 (and NVFP4, see k_gu1_fp4) experts on the
+// block-scaled matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4, with no weight
+// decode on the VALU, and the single-token MXFP4 down projection.
 //
 // The MXFP4 weights (e2m1 codes, one e8m0 scale per 32 along K: DeepSeek-V4-Flash
 // W4A16-FP8 model card, "Architecture & precision") are the instruction's FP4
@@ -73,7 +74,28 @@ struct MxStage {
   uint8_t sc[2][MX_KMAX / 32];
 };
 
-__global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
+// NVFP4 (e2m1 codes, an E4M3 scale per 16 along K and an fp32 scale_2 per expert
+// tensor: DeepSeek-V4-Flash NVFP4 checkpoint card, "Format") in the same
+// instruction. Its block scale is not a power of two and its blocks are 16 wide,
+// so it cannot be the instruction's B scale (B scale code 127, i.e. 1). Instead
+// each row of A holds one term of x on one 16-block of the 128-wide step and zeros
+// elsewhere: row m = 8 t + d is term t on block d (K = 32 (d & 3) + 16 (d >> 2) ...
+// in the instruction's K order; see nv_row_piece). Output row m is then the
+// unscaled dot of that 16-block alone, and the lane holding it multiplies it by the
+// block's E4M3 scale before adding it up. Lane (column n, q) holds output rows
+// 4q .. 4q + 3, i.e. blocks d = 4 (q & 1) + r of term q >> 1, whose four E4M3
+// bytes are one 32-bit word of row n's scale plane. scale_2 multiplies the sum.
+//
+// A lane (row m, group g) holds step bytes 16g + [0, 16) (registers 0-3) and
+// 64 + 16g + [0, 16) (registers 4-7); block d of the step is bytes 16d + [0, 16) of
+// x's 128 values in the order the B operand uses (32g + [0, 32) per lane group,
+// low nibble first), so row m's 16 bytes sit in lane group d & 3, low half if
+// d < 4. (For MXFP4 the K-block of the scale is what matters and the rows are just
+// the terms.)
+
+template <int FMT>
+__global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
+  constexpr bool NV = FMT == FMT_NVFP4;
   __shared__ MxStage st;
   __shared__ float red[MX_WAVES][2][16];
 
@@ -87,8 +109,9 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
   const bool ok = e >= 0 && e < P.n_experts;
 
   // The token's values first (the conversion below waits only for them), then every
-  // weight load of the wave; steps past the wave's last re-read it and are not used. Thread t converts values 16t .. 16t + 15 (two
-  // threads per 32-block; K <= 4096 = 16 x 256); threads past K re-read the last 16.
+  // weight load of the wave; steps past the wave's last re-read it and are not used.
+  // Thread t converts values 16t .. 16t + 15 (two threads per 32-block; K <= 4096 =
+  // 16 x 256); threads past K re-read the last 16.
   const int k0 = min(16 * (int)threadIdx.x, K - 16);
   const uint16_t* xr = reinterpret_cast<const uint16_t*>(P.act) + k0;
   const u32x4 v0 = ld16(xr), v1 = ld16(xr + 8);
@@ -96,12 +119,15 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
   const int n = lane & 15, g = lane >> 4;
   const int rn = min(n0 + n, P.rows - 1);
   const int ec = ok ? e : 0;
+  // NVFP4 scale_2 of both tensors now (uniform loads), not after the last barrier.
+  const float s2g = NV ? P.w[0].scale2[ec] : 1.f, s2u = NV ? P.w[1].scale2[ec] : 1.f;
   const uint8_t* wd[2];
   const uint8_t* ws[2];
+  constexpr int SPB = NV ? 8 : 4;  // scale bytes per 128-wide step
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     wd[mt] = P.w[mt].data + (size_t)ec * P.w[mt].estride + (size_t)rn * (K / 2);
-    ws[mt] = P.w[mt].scales + (size_t)ec * P.w[mt].sestride + (size_t)rn * (K / 32);
+    ws[mt] = P.w[mt].scales + (size_t)ec * P.w[mt].sestride + (size_t)rn * (K / 128 * SPB);
   }
   // Wave w takes the contiguous K steps [w spw, (w + 1) spw): consecutive steps of
   // one wave complete each other's 128-byte lines.
@@ -109,12 +135,16 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
   const int s0 = wave * spw;
   const int my_steps = max(0, min(spw, nsteps - s0));  // uniform per wave
   u32x4 q[2][MX_STEPS];
-  u32x4 sbv4[2][MX_STEPS / 4];  // chunk scales 4 s0 .. 4 s0 + 31 of row rn: dword i = step s0 + i
+  // Scale runs of row rn for the wave's steps, 16 bytes at a time: MXFP4 dword i =
+  // step s0 + i (four e8m0 bytes); NVFP4 dwords 2i, 2i + 1 = step s0 + i (eight E4M3
+  // bytes). Every valid run lies inside the row (my_steps is a multiple of 4).
+  constexpr int NSB = MX_STEPS * SPB / 16;
+  u32x4 sbv4[2][NSB];
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
 #pragma unroll
-    for (int j = 0; j < MX_STEPS / 4; j++)
-      sbv4[mt][j] = ld16(ws[mt] + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
+    for (int j = 0; j < NSB; j++)
+      sbv4[mt][j] = ld16(ws[mt] + (size_t)min(SPB * s0 + 16 * j, SPB * nsteps - 16));
   }
   // Step i's chunk of row rn (steps past the wave's last re-read that one).
   auto load_step = [&](int i) {
@@ -172,19 +202,35 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
   __syncthreads();
 
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  float accn[2] = {0.f, 0.f};  // NVFP4: this lane's scaled block sums
 #pragma unroll
   for (int i = 0; i < MX_STEPS; i++) {
-    if (i + MX_DEPTH < MX_STEPS) load_step(i + MX_DEPTH);  // keep MX_DEPTH steps in flight
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MX_DEPTH < MX_STEPS) {
+      if (i + MX_DEPTH < MX_STEPS) load_step(i + MX_DEPTH);  // keep MX_DEPTH steps in flight
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (i < my_steps) {
       const int s = s0 + i;
-      // A row n < 2 is term n of x (hi, lo); rows 2-15 are zero with scale code 0.
       u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
       int sa = 0;
-      if (n < 2) {
-        a0 = *reinterpret_cast<const u32x4*>(&st.code[n][128 * s + 16 * g]);
-        a1 = *reinterpret_cast<const u32x4*>(&st.code[n][128 * s + 64 + 16 * g]);
-        sa = st.sc[n][4 * s + g];
+      if constexpr (!NV) {
+        // A row n < 2 is term n of x (hi, lo); rows 2-15 are zero with scale code 0.
+        if (n < 2) {
+          a0 = *reinterpret_cast<const u32x4*>(&st.code[n][128 * s + 16 * g]);
+          a1 = *reinterpret_cast<const u32x4*>(&st.code[n][128 * s + 64 + 16 * g]);
+          sa = st.sc[n][4 * s + g];
+        }
+      } else {
+        // nv_row_piece: row n = 8t + d carries term t on block d, whose 16 bytes are
+        // lane group d & 3's low (d < 4) or high half; the scale is term t's e8m0
+        // of the lane group's own K-block (it multiplies zeros elsewhere).
+        const int t = n >> 3, d = n & 7;
+        sa = st.sc[t][4 * s + g];
+        if ((d & 3) == g) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&st.code[t][128 * s + 16 * d]);
+          if (d < 4) a0 = v;
+          else a1 = v;
+        }
       }
       const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -192,16 +238,41 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
         // only the low four registers of an FP4 operand are read
         const i32x8_t bv =
             __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
-        const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));  // this lane's chunk scale, low byte
-        acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
+        if constexpr (!NV) {
+          const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));  // this lane's chunk scale, low byte
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
+        } else {
+          const f32x4_t c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              av, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, sa, 0, 127);
+          // E4M3 scales of blocks 4 (q & 1) + r of step s: one word (q = g here)
+          const uint32_t sw = sbv4[mt][i >> 1][2 * (i & 1) + (g & 1)];
+          const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+          const f32x2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, true);
+          accn[mt] = __builtin_fmaf(s01[0], c[0], accn[mt]);
+          accn[mt] = __builtin_fmaf(s01[1], c[1], accn[mt]);
+          accn[mt] = __builtin_fmaf(s23[0], c[2], accn[mt]);
+          accn[mt] = __builtin_fmaf(s23[1], c[3], accn[mt]);
+        }
       }
     }
   }
   // Prefetches past the wave's last step are never used: let them land first.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (lane < 16) {  // output rows 0 and 1: the hi and lo products
-    red[wave][0][lane] = acc[0][0] + acc[0][1];
-    red[wave][1][lane] = acc[1][0] + acc[1][1];
+  if constexpr (!NV) {
+    if (lane < 16) {  // output rows 0 and 1: the hi and lo products
+      red[wave][0][lane] = acc[0][0] + acc[0][1];
+      red[wave][1][lane] = acc[1][0] + acc[1][1];
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {  // the four lane groups of column n
+      accn[mt] += __shfl_xor(accn[mt], 16, 64);
+      accn[mt] += __shfl_xor(accn[mt], 32, 64);
+    }
+    if (lane < 16) {
+      red[wave][0][lane] = accn[0];
+      red[wave][1][lane] = accn[1];
+    }
   }
   __syncthreads();
   if (threadIdx.x < 16) {
@@ -211,6 +282,8 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_mx4(GemvParams P) {
       gs += red[w][0][threadIdx.x];
       us += red[w][1][threadIdx.x];
     }
+    gs *= s2g;  // 1 for MXFP4
+    us *= s2u;
     const int r = n0 + (int)threadIdx.x;
     if (r < P.rows) P.out[(size_t)slot * P.rows + r] = ok ? silu_mul(gs, us) : 0.f;
     if (!ok && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(P.err, 1u);
@@ -380,11 +453,12 @@ hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gu1_mx4(const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev) {
-  if (!gu1_mx4_fits(p.rows, p.cols)) return hipErrorInvalidValue;
+hipError_t launch_gu1_fp4(int fmt, const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev) {
+  if (!gu1_mx4_fits(p.rows, p.cols) || (fmt != FMT_MXFP4 && fmt != FMT_NVFP4)) return hipErrorInvalidValue;
   dim3 g((unsigned)((p.rows + 15) / 16), (unsigned)n_slots), b(64 * MX_WAVES);
-  if (ev) hipExtLaunchKernelGGL(k_gu1_mx4, g, b, 0, s, ev->start, ev->stop, 0, p);
-  else hipLaunchKernelGGL(k_gu1_mx4, g, b, 0, s, p);
+  auto k = fmt == FMT_NVFP4 ? k_gu1_fp4<FMT_NVFP4> : k_gu1_fp4<FMT_MXFP4>;
+  if (ev) hipExtLaunchKernelGGL(k, g, b, 0, s, ev->start, ev->stop, 0, p);
+  else hipLaunchKernelGGL(k, g, b, 0, s, p);
   return hipGetLastError();
 }
 

@@ -132,8 +132,8 @@ bool fused1_supported(int fg, int fd, int hidden, int inter, int top_k);
 hipError_t launch_fused1(int fg, int fd, const FusedParams& p, hipStream_t s);
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int n_slots, hipStream_t s);
 bool gu1_mx4_fits(int rows, int cols);  // cols % 512 == 0, cols <= 4096
-// Single-token gate/up + SwiGLU for MXFP4 on the block-scaled matrix instruction.
-hipError_t launch_gu1_mx4(const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev);
+// Single-token gate/up + SwiGLU for MXFP4 or NVFP4 on the block-scaled matrix instruction.
+hipError_t launch_gu1_fp4(int fmt, const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev);
 bool down1_mx4_fits(int rows, int cols, int top_k);  // cols % 512 == 0, cols <= 2048, top_k <= 8
 // Single-token down + weighted combine for MXFP4 on the block-scaled matrix instruction.
 hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s);

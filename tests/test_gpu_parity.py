@@ -190,6 +190,8 @@ SMALL = [
     (1, 1, 512, 128, 3, 2),     # ... and a single wave of K steps
     (1, 1, 1024, 512, 16, 8),   # bs=1 MXFP4 down on the matrix unit with its largest work-group (8 slots)
     (1, 1, 1024, 512, 16, 10),  # more slots than it takes: the GEMV path
+    (2, 1, 1536, 288, 4, 2),    # bs=1 NVFP4 gate/up on the matrix unit: the fourth wave gets no K step
+    (2, 1, 512, 128, 3, 2),     # ... and a single wave of K steps
 ]
 
 
@@ -246,12 +248,13 @@ def test_iq2_grouped_gate_up(T, I):
     assert rel_err(h[ok], ref_h[ok]) < TOL
 
 
-def test_mxfp4_gate_up_scale_alignment():
-    """Single-token MXFP4 gate/up reads its chunk scales 16 bytes at a time on the
-    matrix-instruction path; scale planes only 4-byte aligned (the minimum the ABI
-    asks for) take the GEMV path instead. Both must match the oracle."""
-    say("mxfp4 scale alignment")
-    spec = workloads.LayerSpec(1024, 512, 8, 3, mq.FMT_MXFP4, mq.FMT_MXFP4, seed=4501)
+@pytest.mark.parametrize("fmt", [mq.FMT_MXFP4, mq.FMT_NVFP4])
+def test_fp4_gate_up_scale_alignment(fmt):
+    """Single-token MXFP4 / NVFP4 gate/up reads its block scales 16 bytes at a time
+    on the matrix-instruction path; scale planes only 4-byte aligned (the minimum the
+    ABI asks for) take the GEMV path instead. Both must match the oracle."""
+    say("fp4 scale alignment", fmt)
+    spec = workloads.LayerSpec(1024, 512, 8, 3, fmt, mq.FMT_MXFP4, seed=4501)
     layer = upload_layer(spec)
     ids, rw = synth.uniform_routing(spec.seed, 1, 8, 3)
     x = synth.activations_bf16(spec.seed + 1, 1, 1024)
