@@ -182,11 +182,20 @@ GemvParams gemv_params(const moeq_layer* L, const moeq_weight& a, const moeq_wei
 #ifndef MOEQ_GROUPED_WIDE_FROM
 #define MOEQ_GROUPED_WIDE_FROM 2.5
 #endif
-bool grouped_wide(const moeq_layer* L, int T) {
+double pairs_per_expert(const moeq_layer* L, int T) {
   const double E = L->n_experts, K = L->top_k;
   const double touched = E * (1.0 - std::pow(1.0 - K / E, (double)T));
-  return (double)T * K / (touched > 1.0 ? touched : 1.0) >= MOEQ_GROUPED_WIDE_FROM;
+  return (double)T * K / (touched > 1.0 ? touched : 1.0);
 }
+bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >= MOEQ_GROUPED_WIDE_FROM; }
+
+// Q2_K down partials on the matrix instruction (decode once per 16 tokens) from
+// this many expected pairs per touched expert; below it most of a 16-token tile is
+// padding and the GEMV is faster (measured at 1.2 and 1.9 pairs: 415 vs 328 us and
+// 1199 vs 1159 us per layer; at 48 pairs the down took 4.5 ms against 11.3 ms).
+#ifndef MOEQ_DN_Q2K_FROM
+#define MOEQ_DN_Q2K_FROM 8.0
+#endif
 
 int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
                 hipStream_t s, const LaunchEvents* ev = nullptr) {
@@ -235,7 +244,12 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
   p.out = partial;
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
-  int rc = hip_rc(launch_gemv(L->down.fmt, EPI_PARTIAL, p, slots, grouped_wide(L, T) ? 2 : 1, s));
+  int rc;
+  if (L->down.fmt == MOEQ_FMT_Q2_K && pairs_per_expert(L, T) >= MOEQ_DN_Q2K_FROM &&
+      dn_q2k_fits(L->hidden, L->inter, (long)T * L->top_k))
+    rc = hip_rc(launch_dn_q2k(p, slots, s));
+  else
+    rc = hip_rc(launch_gemv(L->down.fmt, EPI_PARTIAL, p, slots, grouped_wide(L, T) ? 2 : 1, s));
   if (rc) return rc;
   return hip_rc(launch_combine(partial, T, L->top_k, L->hidden, y, s));
 }

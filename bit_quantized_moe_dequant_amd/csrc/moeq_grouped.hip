@@ -177,16 +177,15 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
     }
     // The final prefetch is never used: let it land before the registers are reused.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // Lane: weight row n0 + n, tokens m0 + 4g + r.
+    // Lane: weight row n0 + n, tokens m0 + 4g + r, whose pair lane 4g + r read for
+    // operand A (taken while every lane is active; no loads after the arithmetic).
+    int pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) pr[r] = __shfl(pa, 4 * g + r, 64);
     if (n0 + n < P.rows) {
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int m = m0 + 4 * g + r;
-        if (m < M) {
-          const int pair = P.route.perm()[pstart + m];
-          P.out[(size_t)pair * P.rows + n0 + n] = silu_mul(acc[0][r], acc[1][r]);
-        }
-      }
+      for (int r = 0; r < 4; r++)
+        if (m0 + 4 * g + r < M) P.out[(size_t)pr[r] * P.rows + n0 + n] = silu_mul(acc[0][r], acc[1][r]);
     }
   }
 }
@@ -301,11 +300,11 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
 
   for (int m0 = 0; m0 < M; m0 += 16 * GW_NT) {
     const int nt = min(GW_NT, (M - m0 + 15) / 16);  // uniform
-    int x_off[GW_NT];
+    int x_off[GW_NT], pa[GW_NT];
 #pragma unroll
     for (int ti = 0; ti < GW_NT; ti++) {
-      const int pa = P.route.perm()[pstart + min(m0 + 16 * ti + n, M - 1)];
-      x_off[ti] = (pa / P.top_k) * P.cols * 2 + 16 * g;
+      pa[ti] = P.route.perm()[pstart + min(m0 + 16 * ti + n, M - 1)];
+      x_off[ti] = (pa[ti] / P.top_k) * P.cols * 2 + 16 * g;
     }
     f32x4_t acc[GW_NT][2];
 #pragma unroll
@@ -323,17 +322,177 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
       if (sb + 2 >= nsb) break;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // pairs of tokens 16 ti + 4g + r from lane 4g + r, as in k_gu_iq2
+    int pr[GW_NT][4];
+#pragma unroll
+    for (int ti = 0; ti < GW_NT; ti++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) pr[ti][r] = __shfl(pa[ti], 4 * g + r, 64);
     if (n0 + n < P.rows) {
 #pragma unroll
       for (int ti = 0; ti < GW_NT; ti++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const int m = m0 + 16 * ti + 4 * g + r;
-          if (ti < nt && m < M) {
-            const int pair = P.route.perm()[pstart + m];
-            P.out[(size_t)pair * P.rows + n0 + n] = silu_mul(acc[ti][0][r], acc[ti][1][r]);
-          }
-        }
+        for (int r = 0; r < 4; r++)
+          if (ti < nt && m0 + 16 * ti + 4 * g + r < M)
+            P.out[(size_t)pr[ti][r] * P.rows + n0 + n] = silu_mul(acc[ti][0][r], acc[ti][1][r]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- Q2_K down, token-grouped
+// The down projection of Q2_K experts for batches (T > 1), on
+// v_mfma_f32_16x16x16_bf16: the weights of a sub-block are decoded once per group
+// of up to 16 of the expert's tokens instead of once per (token, expert) pair.
+//
+// Q2_K (IQ2_XXS + Q2_K + FP8 hybrid card, format table; block layout: 256 weights
+// in 16 sub-blocks of 16, a 4-bit scale and a 4-bit min per sub-block, fp16 d and
+// dmin per 256): w = d sc q - dmin m with a 2-bit code q. The sub-block is 16 wide,
+// so one instruction (K = 16) covers exactly one sub-block and its fp32 partial can
+// take the sub-block's scale in the lane that holds it.
+//
+// Operands, as in k_gu_iq2: the weights are operand B (16 columns = 16 weight rows),
+// the tokens operand A (16 rows = up to 16 tokens); output lane L register r is
+// token 4(L/16) + r, weight row L % 16. Lane (row n, group g) takes weights
+// 4g .. 4g + 3 of every sub-block: in the device layout these are dword g of the
+// sub-block's 16-byte chunk, at the sub-block's crumb position p. OR-ed into the
+// mantissa of 1.0 a crumb gives the exact bf16 value 1 + q / F (F = 128, 32, 8, 4
+// for p = 0 .. 3), two weights per register in the K order (0, 2), (1, 3); the
+// fp32 h is split into bf16 hi + lo pairs in the same order. With C the
+// instruction's result for that B and H the same for B = 1 (the token's sub-block
+// sum), C - H = (sum h q) / F, and the token's output gets
+//   d sc F (C - H) - dmin m H
+// per sub-block: every product is exact and only the fp32 accumulation rounds.
+// Outputs are route-weighted partials per (pair, row), added by the combine.
+struct GqBuf {
+  uint32_t w[4];   // dword g of each 16-byte chunk of the superblock, row n
+  u32x4 sc;        // the 16 sub-block scale/min bytes of row n
+  uint32_t dd;     // d | dmin << 16
+  u32x4 x[16];     // token (A row) m's h at K = 16 j + 4g .. + 3, sub-block j
+};
+
+struct GqStreams {
+  __amdgpu_buffer_rsrc_t w, s, x;
+  int w_off, s_off, x_off;  // lane byte offsets: row rn's data and scales; token row + group g
+};
+
+__device__ __forceinline__ void gq_issue(const GqStreams& st, int sb, GqBuf& b) {
+#pragma unroll
+  for (int c = 0; c < 4; c++) b.w[c] = __builtin_amdgcn_raw_buffer_load_b32(st.w, st.w_off + 16 * c, sb * 64, 0);
+  b.sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.s, st.s_off, sb * 20, 0));
+  b.dd = __builtin_amdgcn_raw_buffer_load_b32(st.s, st.s_off + 16, sb * 20, 0);
+#pragma unroll
+  for (int j = 0; j < 16; j++)
+    b.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, st.x_off + 64 * j, sb * 1024, 0));
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4_t gq_pair(uint32_t a, uint32_t b) { return __builtin_bit_cast(s16x4_t, u32x2{a, b}); }
+
+__device__ __forceinline__ void gq_compute(const GqBuf& b, f32x4_t& acc) {
+  const uint32_t ONE = 0x3F803F80u;
+  const s16x4_t ones = gq_pair(ONE, ONE);
+  const float d = half_bits_f32(b.dd), dmin = half_bits_f32(b.dd >> 16);
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const uint32_t w = b.w[c], w8 = b.w[c] >> 8;
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      const int j = 8 * (c >> 1) + (c & 1) + 2 * p;  // the sub-block at chunk c, crumb p
+      // B: 1 + q / F for weights (4g, 4g + 2) and (4g + 1, 4g + 3)
+      uint32_t ba, bb;
+      if (p < 3) {
+        const uint32_t m = 0x00030003u << (2 * p);
+        ba = (w & m) | ONE;
+        bb = (w8 & m) | ONE;
+      } else {
+        ba = ((w >> 1) & 0x00600060u) | ONE;
+        bb = ((w8 >> 1) & 0x00600060u) | ONE;
+      }
+      const s16x4_t bv = gq_pair(ba, bb);
+      // A: the token's h at K = 16 j + 4g + (0, 2, 1, 3) as bf16 hi and lo
+      uint32_t h0, l0, h1, l1;
+      split_pair(u2f(b.x[j][0]), u2f(b.x[j][2]), h0, l0);
+      split_pair(u2f(b.x[j][1]), u2f(b.x[j][3]), h1, l1);
+      const s16x4_t ah = gq_pair(h0, h1), al = gq_pair(l0, l1);
+      f32x4_t cq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      cq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bv, cq, 0, 0, 0);
+      f32x4_t ch = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      ch = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, ones, ch, 0, 0, 0);
+      const uint32_t byte = (b.sc[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      constexpr float F[4] = {128.f, 32.f, 8.f, 4.f};
+      const float cs = d * F[p] * (float)(byte & 15u);  // d sc F: exact (11 x 4 bits, power of two)
+      const float cm = dmin * (float)(byte >> 4);       // exact
+#pragma unroll
+      for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(cs, cq[r] - ch[r], __builtin_fmaf(-cm, ch[r], acc[r]));
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_dn_q2k(GemvParams P) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int slot = blockIdx.y;
+  if (slot >= P.route.n_slots()[0]) return;
+  const int e = P.route.slots()[slot];
+  const int pstart = P.route.offsets()[e];
+  const int M = P.route.offsets()[e + 1] - pstart;
+  const int n0 = blockIdx.x * GI_ROWS + wave * 16;
+  if (n0 >= P.rows || M <= 0) return;
+
+  if (e < 0 || e >= P.n_experts) {
+    // Out-of-range expert id (its bucket): its pairs contribute nothing.
+    for (int m = 0; m < M; m++) {
+      const int pair = P.route.perm()[pstart + m];
+      if (lane < 16 && n0 + lane < P.rows) P.out[(size_t)pair * P.rows + n0 + lane] = 0.f;
+    }
+    return;
+  }
+
+  const int nsb = P.cols / 256;
+  const int rn = min(n0 + n, P.rows - 1);
+  GqStreams st;
+  st.w = gi_buffer(P.w[0].data + (size_t)e * P.w[0].estride);
+  st.s = gi_buffer(P.w[0].scales + (size_t)e * P.w[0].sestride);
+  st.x = gi_buffer(P.act);
+  st.w_off = rn * nsb * 64 + 4 * g;
+  st.s_off = rn * nsb * 20;
+
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    // Pair of operand-A row n (lanes past the expert's last token repeat it).
+    const int pa = P.route.perm()[pstart + min(m0 + n, M - 1)];
+    st.x_off = pa * P.cols * 4 + 16 * g;
+    // Its route weight; the outputs of token 4g + r take both from lane 4g + r.
+    const float rwa = P.rw[pa];
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    GqBuf A, B;
+    gq_issue(st, 0, A);
+    for (int sb = 0;; sb += 2) {
+      gq_issue(st, min(sb + 1, nsb - 1), B);
+      __builtin_amdgcn_sched_barrier(0);
+      gq_compute(A, acc);
+      if (sb + 1 >= nsb) break;
+      gq_issue(st, min(sb + 2, nsb - 1), A);
+      __builtin_amdgcn_sched_barrier(0);
+      gq_compute(B, acc);
+      if (sb + 2 >= nsb) break;
+    }
+    // The final prefetch is never used: let it land before the registers are reused.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Lane: weight row n0 + n, tokens m0 + 4g + r (pair and route weight from lane
+    // 4g + r, read while every lane is active).
+    int pr[4];
+    float wr[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      pr[r] = __shfl(pa, 4 * g + r, 64);
+      wr[r] = __shfl(rwa, 4 * g + r, 64);
+    }
+    if (n0 + n < P.rows) {
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (m0 + 4 * g + r < M) P.out[(size_t)pr[r] * P.rows + n0 + n] = acc[r] * wr[r];
     }
   }
 }
@@ -351,6 +510,20 @@ hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, bool wide, hipStream_
   dim3 g((unsigned)((p.rows + GI_ROWS - 1) / GI_ROWS), (unsigned)n_slots);
   if (wide) hipLaunchKernelGGL(k_gu_iq2_wide, g, dim3(64 * GI_WAVES), 0, s, p);
   else hipLaunchKernelGGL(k_gu_iq2, g, dim3(64 * GI_WAVES), 0, s, p);
+  return hipGetLastError();
+}
+
+// K a multiple of 256; the raw buffer offsets of an expert's planes and of the
+// activations stay below 2^31.
+bool dn_q2k_fits(int rows, int cols, long pairs) {
+  return rows > 0 && cols > 0 && cols % 256 == 0 && (long)rows * (cols / 256) * 64 < (1L << 31) &&
+         pairs * cols * 4 < (1L << 31);
+}
+
+hipError_t launch_dn_q2k(const GemvParams& p, int n_slots, hipStream_t s) {
+  if (!dn_q2k_fits(p.rows, p.cols, (long)p.T * p.top_k)) return hipErrorInvalidValue;
+  dim3 g((unsigned)((p.rows + GI_ROWS - 1) / GI_ROWS), (unsigned)n_slots);
+  hipLaunchKernelGGL(k_dn_q2k, g, dim3(64 * GI_WAVES), 0, s, p);
   return hipGetLastError();
 }
 

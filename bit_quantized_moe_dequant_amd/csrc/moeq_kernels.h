@@ -137,6 +137,10 @@ hipError_t launch_gu1_fp4(int fmt, const GemvParams& p, int n_slots, hipStream_t
 bool down1_mx4_fits(int rows, int cols, int top_k);  // cols % 512 == 0, cols <= 2048, top_k <= 8
 // Single-token down + weighted combine for MXFP4 on the block-scaled matrix instruction.
 hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s);
+// Token-grouped Q2_K down (T > 1) on the bf16 matrix instruction: route-weighted
+// partials [pairs][rows] for the combine.
+bool dn_q2k_fits(int rows, int cols, long pairs);
+hipError_t launch_dn_q2k(const GemvParams& p, int n_slots, hipStream_t s);
 bool gu_iq2_fits(int rows, int cols);  // cols % 256 == 0
 // Grouped gate/up + SwiGLU for IQ2_XXS on the bf16 matrix instruction (T > 1).
 // wide: decode each superblock once for two 16-token tiles (many tokens per expert).

@@ -250,6 +250,34 @@ def test_iq2_grouped_gate_up(T, I):
     assert rel_err(h[ok], ref_h[ok]) < TOL
 
 
+@pytest.mark.parametrize("T,H", [(40, 544), (9, 512)])
+def test_q2k_grouped_down(T, H):
+    """Q2_K down for T > 1 (the matrix-instruction path, taken from 8 pairs per
+    expert): with two experts and top-2 every expert gets all T tokens, so T = 40
+    spans three 16-token tiles (the last partial) and T = 9 one partial tile;
+    H = 544 leaves the last 64-row work-group half empty; one out-of-range
+    id puts a pair in the invalid bucket, which must add nothing to y. The down stage
+    is fed the oracle's own h, so y is compared with the oracle's y directly."""
+    say("q2k grouped down", T, H)
+    spec = workloads.LayerSpec(H, 256, 2, 2, mq.FMT_MXFP4, mq.FMT_Q2_K, seed=4600 + T)
+    layer = upload_layer(spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, 2, 2)
+    x = synth.activations_bf16(spec.seed + 1, T, H)
+    rw0 = rw.copy()
+    rw0[1, 0] = 0.0  # the pair whose id goes out of range contributes nothing
+    ref_y, ref_h = moe.moe_layer(x, ids, rw0, oracle_weight_fn(spec))
+    bad = ids.copy()
+    bad[1, 0] = 99
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    it = cuda(bad)
+    mq.route(layer, it, ws=ws)
+    h = torch.from_numpy(np.ascontiguousarray(ref_h, dtype=np.float32)).cuda()
+    y = mq.down(layer, h, it, cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    assert rel_err(y, ref_y) < TOL
+
+
 @pytest.mark.parametrize("fmt", [mq.FMT_MXFP4, mq.FMT_NVFP4])
 def test_fp4_gate_up_scale_alignment(fmt):
     """Single-token MXFP4 / NVFP4 gate/up reads its block scales 16 bytes at a time
