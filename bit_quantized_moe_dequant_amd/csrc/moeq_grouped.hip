@@ -356,42 +356,58 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
 // 4g .. 4g + 3 of every sub-block: in the device layout these are dword g of the
 // sub-block's 16-byte chunk, at the sub-block's crumb position p. OR-ed into the
 // mantissa of 1.0 a crumb gives the exact bf16 value 1 + q / F (F = 128, 32, 8, 4
-// for p = 0 .. 3), two weights per register in the K order (0, 2), (1, 3); the
-// fp32 h is split into bf16 hi + lo pairs in the same order. With C the
-// instruction's result for that B and H the same for B = 1 (the token's sub-block
-// sum), C - H = (sum h q) / F, and the token's output gets
+// for p = 0 .. 3), two weights per register in the K order (0, 2), (1, 3). With C
+// the instruction's result and H the token's sub-block sum of the same bf16 h
+// values, C - H = (sum h q) / F, and the token's output gets
 //   d sc F (C - H) - dmin m H
-// per sub-block: every product is exact and only the fp32 accumulation rounds.
-// Outputs are route-weighted partials per (pair, row), added by the combine.
-struct GqBuf {
-  uint32_t w[4];   // dword g of each 16-byte chunk of the superblock, row n
-  u32x4 sc;        // the 16 sub-block scale/min bytes of row n
-  uint32_t dd;     // d | dmin << 16
-  u32x4 x[16];     // token (A row) m's h at K = 16 j + 4g .. + 3, sub-block j
+// per sub-block: every product is exact and only fp32 sums round.
+//
+// The work-group's four waves (64 weight rows) share the token tile: per
+// superblock its h is staged once in LDS, already split into bf16 hi + lo pairs in
+// the instructions' K order, with the sums H (one (token, sub-block) per thread),
+// in two buffers with one barrier per superblock; the loads run two superblocks
+// ahead. Outputs are route-weighted partials per (pair, row), added by the combine.
+struct GqStage {
+  u32x4 a[16 * 16 * 4];  // [(sub-block j * 16 + token m) * 4 + group g]: hi (K 0,2), hi (1,3), lo, lo
+  float h[16 * 16];      // [sub-block j * 16 + token m]: sum of the 16 bf16 (hi + lo) values
 };
 
-struct GqStreams {
-  __amdgpu_buffer_rsrc_t w, s, x;
-  int w_off, s_off, x_off;  // lane byte offsets: row rn's data and scales; token row + group g
+struct GqW {
+  uint32_t w[4];  // dword g of each 16-byte chunk of the superblock, row n
+  u32x4 sc;       // the 16 sub-block scale/min bytes of row n
+  uint32_t dd;    // d | dmin << 16
 };
-
-__device__ __forceinline__ void gq_issue(const GqStreams& st, int sb, GqBuf& b) {
-#pragma unroll
-  for (int c = 0; c < 4; c++) b.w[c] = __builtin_amdgcn_raw_buffer_load_b32(st.w, st.w_off + 16 * c, sb * 64, 0);
-  b.sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.s, st.s_off, sb * 20, 0));
-  b.dd = __builtin_amdgcn_raw_buffer_load_b32(st.s, st.s_off + 16, sb * 20, 0);
-#pragma unroll
-  for (int j = 0; j < 16; j++)
-    b.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, st.x_off + 64 * j, sb * 1024, 0));
-}
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ s16x4_t gq_pair(uint32_t a, uint32_t b) { return __builtin_bit_cast(s16x4_t, u32x2{a, b}); }
 
-__device__ __forceinline__ void gq_compute(const GqBuf& b, f32x4_t& acc) {
+__device__ __forceinline__ void gq_wload(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr, int w_off, int s_off,
+                                         int sb, GqW& b) {
+#pragma unroll
+  for (int c = 0; c < 4; c++) b.w[c] = __builtin_amdgcn_raw_buffer_load_b32(wr, w_off + 16 * c, sb * 64, 0);
+  b.sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off, sb * 20, 0));
+  b.dd = __builtin_amdgcn_raw_buffer_load_b32(sr, s_off + 16, sb * 20, 0);
+}
+
+// This thread's (token, sub-block): 16 fp32 h values -> LDS as bf16 hi/lo pairs and
+// their sum.
+__device__ __forceinline__ void gq_stage_write(const u32x4 (&v)[4], int tm, int tj, GqStage& s) {
+  float hsum = 0.f;
+#pragma unroll
+  for (int g = 0; g < 4; g++) {
+    uint32_t h0, l0, h1, l1;
+    split_pair(u2f(v[g][0]), u2f(v[g][2]), h0, l0);
+    split_pair(u2f(v[g][1]), u2f(v[g][3]), h1, l1);
+    s.a[(tj * 16 + tm) * 4 + g] = u32x4{h0, h1, l0, l1};
+    hsum += (u2f(h0 << 16) + u2f(l0 << 16)) + (u2f(h0 & 0xFFFF0000u) + u2f(l0 & 0xFFFF0000u)) +
+            (u2f(h1 << 16) + u2f(l1 << 16)) + (u2f(h1 & 0xFFFF0000u) + u2f(l1 & 0xFFFF0000u));
+  }
+  s.h[tj * 16 + tm] = hsum;
+}
+
+__device__ __forceinline__ void gq_compute(const GqW& b, const GqStage& s, int n, int g, f32x4_t& acc) {
   const uint32_t ONE = 0x3F803F80u;
-  const s16x4_t ones = gq_pair(ONE, ONE);
   const float d = half_bits_f32(b.dd), dmin = half_bits_f32(b.dd >> 16);
 #pragma unroll
   for (int c = 0; c < 4; c++) {
@@ -410,26 +426,25 @@ __device__ __forceinline__ void gq_compute(const GqBuf& b, f32x4_t& acc) {
         bb = ((w8 >> 1) & 0x00600060u) | ONE;
       }
       const s16x4_t bv = gq_pair(ba, bb);
-      // A: the token's h at K = 16 j + 4g + (0, 2, 1, 3) as bf16 hi and lo
-      uint32_t h0, l0, h1, l1;
-      split_pair(u2f(b.x[j][0]), u2f(b.x[j][2]), h0, l0);
-      split_pair(u2f(b.x[j][1]), u2f(b.x[j][3]), h1, l1);
-      const s16x4_t ah = gq_pair(h0, h1), al = gq_pair(l0, l1);
-      f32x4_t cq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      cq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bv, cq, 0, 0, 0);
-      f32x4_t ch = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      ch = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, ones, ch, 0, 0, 0);
+      const u32x4 av = s.a[(j * 16 + n) * 4 + g];  // A row n = token n
+      f32x4_t cq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gq_pair(av[0], av[1]), bv, f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                              0, 0, 0);
+      cq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gq_pair(av[2], av[3]), bv, cq, 0, 0, 0);
+      const f32x4_t hs = *reinterpret_cast<const f32x4_t*>(&s.h[j * 16 + 4 * g]);  // tokens 4g .. 4g + 3
       const uint32_t byte = (b.sc[j >> 2] >> (8 * (j & 3))) & 0xFFu;
       constexpr float F[4] = {128.f, 32.f, 8.f, 4.f};
       const float cs = d * F[p] * (float)(byte & 15u);  // d sc F: exact (11 x 4 bits, power of two)
       const float cm = dmin * (float)(byte >> 4);       // exact
 #pragma unroll
-      for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(cs, cq[r] - ch[r], __builtin_fmaf(-cm, ch[r], acc[r]));
+      for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(cs, cq[r] - hs[r], __builtin_fmaf(-cm, hs[r], acc[r]));
     }
   }
 }
 
-__global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_dn_q2k(GemvParams P) {
+__global__ __launch_bounds__(64 * GI_WAVES) void k_dn_q2k(GemvParams P) {
+  __shared__ GqStage stg[2];
+  __shared__ int s_pair[16];
+  __shared__ float s_rw[16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -438,62 +453,71 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const int e = P.route.slots()[slot];
   const int pstart = P.route.offsets()[e];
   const int M = P.route.offsets()[e + 1] - pstart;
-  const int n0 = blockIdx.x * GI_ROWS + wave * 16;
-  if (n0 >= P.rows || M <= 0) return;
+  const int r0 = blockIdx.x * GI_ROWS;
+  if (r0 >= P.rows || M <= 0) return;  // uniform per work-group: the barriers below are reached by all
 
   if (e < 0 || e >= P.n_experts) {
     // Out-of-range expert id (its bucket): its pairs contribute nothing.
     for (int m = 0; m < M; m++) {
       const int pair = P.route.perm()[pstart + m];
-      if (lane < 16 && n0 + lane < P.rows) P.out[(size_t)pair * P.rows + n0 + lane] = 0.f;
+      for (int i = threadIdx.x; i < GI_ROWS; i += 64 * GI_WAVES)
+        if (r0 + i < P.rows) P.out[(size_t)pair * P.rows + r0 + i] = 0.f;
     }
     return;
   }
 
   const int nsb = P.cols / 256;
+  const int n0 = r0 + wave * 16;
   const int rn = min(n0 + n, P.rows - 1);
-  GqStreams st;
-  st.w = gi_buffer(P.w[0].data + (size_t)e * P.w[0].estride);
-  st.s = gi_buffer(P.w[0].scales + (size_t)e * P.w[0].sestride);
-  st.x = gi_buffer(P.act);
-  st.w_off = rn * nsb * 64 + 4 * g;
-  st.s_off = rn * nsb * 20;
+  const __amdgpu_buffer_rsrc_t wr = gi_buffer(P.w[0].data + (size_t)e * P.w[0].estride);
+  const __amdgpu_buffer_rsrc_t sr = gi_buffer(P.w[0].scales + (size_t)e * P.w[0].sestride);
+  const __amdgpu_buffer_rsrc_t xr = gi_buffer(P.act);
+  const int w_off = rn * nsb * 64 + 4 * g, s_off = rn * nsb * 20;
+  // staging: thread = (token tm, sub-block tj)
+  const int tm = threadIdx.x >> 4, tj = threadIdx.x & 15;
 
   for (int m0 = 0; m0 < M; m0 += 16) {
-    // Pair of operand-A row n (lanes past the expert's last token repeat it).
-    const int pa = P.route.perm()[pstart + min(m0 + n, M - 1)];
-    st.x_off = pa * P.cols * 4 + 16 * g;
-    // Its route weight; the outputs of token 4g + r take both from lane 4g + r.
-    const float rwa = P.rw[pa];
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    GqBuf A, B;
-    gq_issue(st, 0, A);
-    for (int sb = 0;; sb += 2) {
-      gq_issue(st, min(sb + 1, nsb - 1), B);
-      __builtin_amdgcn_sched_barrier(0);
-      gq_compute(A, acc);
-      if (sb + 1 >= nsb) break;
-      gq_issue(st, min(sb + 2, nsb - 1), A);
-      __builtin_amdgcn_sched_barrier(0);
-      gq_compute(B, acc);
-      if (sb + 2 >= nsb) break;
+    const int pt = P.route.perm()[pstart + min(m0 + tm, M - 1)];  // tokens past the last repeat it
+    if (tj == 0) {
+      s_pair[tm] = pt;
+      s_rw[tm] = P.rw[pt];
     }
-    // The final prefetch is never used: let it land before the registers are reused.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // Lane: weight row n0 + n, tokens m0 + 4g + r (pair and route weight from lane
-    // 4g + r, read while every lane is active).
-    int pr[4];
-    float wr[4];
+    const int x_off = pt * P.cols * 4 + 64 * tj;
+    // Two superblocks in flight: register set k holds superblocks k, k + 2, ...
+    // (loads past the last superblock re-read it and are not used).
+    u32x4 v[2][4];
+    GqW W[2];
+    auto xload = [&](int sb, u32x4(&dst)[4]) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      pr[r] = __shfl(pa, 4 * g + r, 64);
-      wr[r] = __shfl(rwa, 4 * g + r, 64);
+      for (int i = 0; i < 4; i++)
+        dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, x_off + 16 * i, sb * 1024, 0));
+    };
+    xload(0, v[0]);
+    gq_wload(wr, sr, w_off, s_off, 0, W[0]);
+    xload(min(1, nsb - 1), v[1]);
+    gq_wload(wr, sr, w_off, s_off, min(1, nsb - 1), W[1]);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < nsb; sb += 2) {
+#pragma unroll
+      for (int k = 0; k < 2; k++) {
+        if (sb + k < nsb) {  // uniform
+          gq_stage_write(v[k], tm, tj, stg[k]);
+          xload(min(sb + k + 2, nsb - 1), v[k]);
+          __syncthreads();
+          gq_compute(W[k], stg[k], n, g, acc);
+          gq_wload(wr, sr, w_off, s_off, min(sb + k + 2, nsb - 1), W[k]);
+        }
+      }
     }
+    // The final prefetches are never used: let them land before the registers are reused.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Lane: weight row n0 + n, tokens m0 + 4g + r.
     if (n0 + n < P.rows) {
 #pragma unroll
       for (int r = 0; r < 4; r++)
-        if (m0 + 4 * g + r < M) P.out[(size_t)pr[r] * P.rows + n0 + n] = acc[r] * wr[r];
+        if (m0 + 4 * g + r < M) P.out[(size_t)s_pair[4 * g + r] * P.rows + n0 + n] = acc[r] * s_rw[4 * g + r];
     }
+    __syncthreads();  // the staging buffers and s_pair / s_rw are rewritten by the next tile
   }
 }
 
