@@ -17,6 +17,7 @@ kernel (the gate/up dequant-GEMV, timed with HIP events on its stream) and a
 workload on this host).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --workload iq2_q2k_43 --tokens 2048   # a batched layer: us/layer only
 """
 from __future__ import annotations
 
@@ -292,12 +293,78 @@ def run_prefill(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def run_batch(args, wl):
+    """A decode workload at T > 1 tokens per step (--tokens): one step = one MoE layer
+    over T tokens with a fresh uniform top-k per token (routing, gate/up, down,
+    combine), K steps captured in one HIP graph. Not the headline metric: it prints
+    us/layer, tokens/s and the weight bytes of the touched experts per second."""
+    import torch
+
+    import bit_quantized_moe_dequant_amd as mq
+    from bit_quantized_moe_dequant_amd import synth, workloads
+
+    spec = wl.spec
+    T, K, W = args.tokens, args.steps, args.warmup
+    log(f"workload {wl.name} at T={T}: building layer ({spec.n_experts} experts) on the device")
+    layer = workloads.build_layer(mq, spec)
+    routes = [synth.uniform_routing(spec.seed + 77 * i, T, spec.n_experts, spec.top_k) for i in range(W + K)]
+    ids_t = [torch.from_numpy(r[0]).cuda() for r in routes]
+    rw_t = [torch.from_numpy(r[1]).cuda() for r in routes]
+    x_t = torch.from_numpy(synth.activations_bf16(spec.seed + 5, T, spec.hidden).view(np.int16)).cuda().view(
+        torch.bfloat16)
+    y = torch.empty((T, spec.hidden), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(T)
+    touched = float(np.mean([np.unique(r[0]).size for r in routes[W:]]))
+    step_bytes = touched * layer.expert_bytes()
+
+    def step(i):
+        mq.expert_forward(layer, x_t, ids_t[i], rw_t[i], y=y, ws=ws)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(W + i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    err = mq.check_device_error(ws)
+    if err:
+        sys.exit(f"device error word {err:#x}")
+    log(f"{K} steps at T={T}: {ms_per_step * 1e3:.1f} us/layer")
+    print(json.dumps({
+        "metric": f"routed-MoE layer us/layer at T={T} (batched decode / prefill, not the headline)",
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us/layer",
+        "higher_is_better": False,
+        "steps": K,
+        "warmup": W,
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "experts_touched": round(touched, 1),
+        "weight_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens_per_step": T, "routing": "uniform top-k per token, fresh per step",
+                   "launch": "HIP graph of the timed steps"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000 decode, 100 prefill)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mxfp4_layer")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="decode workloads: tokens per step (T > 1 prints a separate us/layer line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -325,9 +392,11 @@ def main():
         return
     wl = workloads.WORKLOADS[args.workload]
     if args.steps is None:
-        args.steps = 100 if wl.prefill else 2000
+        args.steps = 100 if wl.prefill else (20 if args.tokens > 1 else 2000)
     if wl.prefill:
         return run_prefill(args, wl)
+    if args.tokens > 1:
+        return run_batch(args, wl)
     spec = wl.spec
     K, W = args.steps, args.warmup
     log(f"workload {wl.name}: building layer ({spec.n_experts} experts) on the device")
