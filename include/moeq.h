@@ -9,10 +9,18 @@
  *   for token t routed to experts e_k with route weights w_k (k < top_k):
  *     h_k = silu(G_e x_t) * (U_e x_t),   y_t = sum_k w_k * (D_e h_k)
  *
- * At decode (few tokens) this is a fused dequantize + GEMV per projection; at
- * prefill with MXFP4 weights it is a token-grouped GEMM on the block-scaled FP4
- * matrix instructions, with activations quantised to MXFP8 (fp4 weights times
- * E4M3 activations: DeepSeekv4 Flash for 1x Spark forum thread, second post).
+ * At decode (few tokens) each projection streams the routed experts' weights
+ * once: MXFP4 and NVFP4 single-token gate/up (and MXFP4 down) feed the FP4 codes
+ * straight into the block-scaled matrix instruction, the other formats and shapes
+ * decode on the VALU (dequantize + GEMV). When many tokens share an expert,
+ * IQ2_XXS gate/up and Q2_K down decode once per 16-token tile for the bf16
+ * matrix instructions. At prefill with MXFP4 weights it is a token-grouped GEMM
+ * on the block-scaled FP4 matrix instructions, with activations quantised to
+ * MXFP8 (fp4 weights times E4M3 activations: DeepSeekv4 Flash for 1x Spark forum
+ * thread, second post). The decode paths agree with the exact layer to the
+ * documented tolerance, the prefill path with the same layer on MXFP8
+ * activations; which path runs depends only on formats, shapes, T and
+ * alignment, never on the data.
  *
  * Conventions for every entry point:
  *  - Pointers named *_host are host memory; every other buffer pointer is device
@@ -164,10 +172,10 @@ int moeq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* y[T][H] (fp32, overwritten) of the routed layer for x[T][H] (bf16), expert ids
  * ids[T][K] (int32) and route weights rw[T][K] (fp32, applied after down as given).
- * Decode path (GEMV, any format) unless T >= 128, gate, up and down are all
- * MXFP4 and the layer meets the prefill stages' shape and alignment conditions
- * (below), in which case the W4A8 prefill path runs (x and h quantised to MXFP8).
- * T == 0 is a no-op. x, y 16-byte aligned. */
+ * Decode path (any format: the stage kernels below) unless T >= 128, gate, up
+ * and down are all MXFP4 and the layer meets the prefill stages' shape and
+ * alignment conditions (below), in which case the W4A8 prefill path runs (x and h
+ * quantised to MXFP8). T == 0 is a no-op. x, y 16-byte aligned. */
 int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y,
                         void* ws, size_t ws_bytes, void* stream);
 
