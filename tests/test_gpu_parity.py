@@ -192,6 +192,7 @@ SMALL = [
     (1, 1, 1024, 512, 16, 10),  # more slots than it takes: the GEMV path
     (1, 1, 1024, 512, 12, 6),   # bs=1 MXFP4 matrix-unit kernels at the full layer's top-6
     (1, 1, 2048, 1024, 8, 2),   # ... and with two slots
+    (2, 3, 2048, 1024, 4, 2),   # NVFP4 gate/up + Q2_K down, intermediate 1024
     (2, 1, 1536, 288, 4, 2),    # bs=1 NVFP4 gate/up on the matrix unit: the fourth wave gets no K step
     (2, 1, 512, 128, 3, 2),     # ... and a single wave of K steps
 ]
