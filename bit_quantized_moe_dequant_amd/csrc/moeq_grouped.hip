@@ -191,11 +191,12 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
 }
 
 // ---------------------------------------------------------------- many tokens per expert
-// Prefill-sized batches: each superblock is decoded once (bf16 words and sub-block
-// scales kept in registers) and applied to GW_NT 16-token tiles per pass, so the
-// decode is shared by up to 16 GW_NT tokens instead of 16. The weights stream
-// through two buffers as above; a pass loads its tiles' activations per
-// superblock, before the decode, so the decode covers their latency.
+// Prefill-sized batches: each sub-block is decoded once and applied to GW_NT
+// 16-token tiles per pass, so the decode is shared by up to 16 GW_NT tokens
+// instead of 16. The pass's activations are staged once per superblock in LDS for
+// the work-group's four waves (each wave reading its own copy from L2 had been
+// half the kernel's time), in two buffers with one barrier per superblock, and the
+// activation and weight loads run two superblocks ahead.
 constexpr int GW_NT = 2;
 
 struct GwBuf {
@@ -213,46 +214,46 @@ __device__ __forceinline__ void gw_issue(const GiStreams& st, int sb, GwBuf& b) 
   }
 }
 
-// One superblock: activations of the pass's tiles, decode, then the multiplies.
-__device__ __forceinline__ void gw_compute(const GiStreams& st, const int (&x_off)[GW_NT], int nt, int sb,
-                                           const GwBuf& b, int g, const Iq2Lds* t, const GiSigns* sg,
-                                           f32x4_t (&acc)[GW_NT][2]) {
-  u32x4 xv[GW_NT][8];
+// The pass's activations for one superblock, shared by the work-group's waves:
+// [((tile * 8 + sub-block) * 16 + token) * 4 + group] = 8 bf16 at K = 32 j + 8 g.
+struct GwStage {
+  u32x4 x[GW_NT * 8 * 16 * 4];
+};
+
+// One superblock: each sub-block is decoded once (both matrices) and applied to
+// the pass's tiles, whose activations come from LDS.
+__device__ __forceinline__ void gw_compute(int nt, const GwBuf& b, const GwStage& xs, int n, int g, const Iq2Lds* t,
+                                           const GiSigns* sg, f32x4_t (&acc)[GW_NT][2]) {
+  float d8[2];
 #pragma unroll
-  for (int ti = 0; ti < GW_NT; ti++)
+  for (int mt = 0; mt < 2; mt++) d8[mt] = half_bits_f32(b.d[mt]) * 0.125f;
 #pragma unroll
-    for (int j = 0; j < 8; j++)
-      xv[ti][j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, x_off[ti] + 64 * j, sb * 512, 0));
-  u32x4 wv[2][8];
-  float db[2][8];
+  for (int j = 0; j < 8; j++) {
+    u32x4 wv[2];
+    float db[2];
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++) {
-    const float d8 = half_bits_f32(b.d[mt]) * 0.125f;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
+    for (int mt = 0; mt < 2; mt++) {
       const uint32_t a0 = b.w[mt][j >> 1][2 * (j & 1)], a1 = b.w[mt][j >> 1][2 * (j & 1) + 1];
       const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
       const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
       const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
       const u32x4 m = sg->w[code];
-      wv[mt][j] = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
-      db[mt][j] = d8 * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
+      wv[mt] = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
+      db[mt] = d8[mt] * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
     }
-  }
 #pragma unroll
-  for (int ti = 0; ti < GW_NT; ti++) {
-    if (ti < nt) {
+    for (int ti = 0; ti < GW_NT; ti++) {
+      if (ti < nt) {
+        const u32x4 xv = xs.x[((ti * 8 + j) * 16 + n) * 4 + g];
 #pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[ti][j]),
-                                                                    __builtin_bit_cast(bf16x8_t, wv[mt][j]),
+        for (int mt = 0; mt < 2; mt++) {
+          const f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                                    __builtin_bit_cast(bf16x8_t, wv[mt]),
                                                                     f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; r++) acc[ti][mt][r] = __builtin_fmaf(c[r], db[mt][j], acc[ti][mt][r]);
+          for (int r = 0; r < 4; r++) acc[ti][mt][r] = __builtin_fmaf(c[r], db[mt], acc[ti][mt][r]);
         }
+      }
     }
   }
 }
@@ -260,6 +261,8 @@ __device__ __forceinline__ void gw_compute(const GiStreams& st, const int (&x_of
 __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_gu_iq2_wide(GemvParams P) {
   __shared__ Iq2Lds lds_tab[1];
   __shared__ GiSigns signs[1];
+  __shared__ GwStage stg[2];
+  __shared__ int s_pair[16 * GW_NT];
   iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
   if (threadIdx.x < 128) {
     uint32_t m[4];
@@ -276,17 +279,19 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const int e = P.route.slots()[slot];
   const int pstart = P.route.offsets()[e];
   const int M = P.route.offsets()[e + 1] - pstart;
-  const int n0 = blockIdx.x * GI_ROWS + wave * 16;
-  if (n0 >= P.rows || M <= 0) return;
+  const int r0 = blockIdx.x * GI_ROWS;
+  if (r0 >= P.rows || M <= 0) return;  // uniform per work-group: the barriers below are reached by all
   if (e < 0 || e >= P.n_experts) {
     for (int m = 0; m < M; m++) {
       const int pair = P.route.perm()[pstart + m];
-      if (lane < 16 && n0 + lane < P.rows) P.out[(size_t)pair * P.rows + n0 + lane] = 0.f;
+      for (int i = threadIdx.x; i < GI_ROWS; i += 64 * GI_WAVES)
+        if (r0 + i < P.rows) P.out[(size_t)pair * P.rows + r0 + i] = 0.f;
     }
     return;
   }
 
   const int nsb = P.cols / 256;
+  const int n0 = r0 + wave * 16;
   const int rn = min(n0 + n, P.rows - 1);
   GiStreams st;
 #pragma unroll
@@ -297,45 +302,55 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
   st.x = gi_buffer(P.act);
   st.w_off = rn * nsb * 64;
   st.s_off = rn * nsb * 2;
+  // staging: thread = (pass token tt, sub-block q); its 64 bytes are the four
+  // 8-value groups of that sub-block
+  const int tt = threadIdx.x >> 3, q = threadIdx.x & 7;
+  const int sidx = (((tt >> 4) * 8 + q) * 16 + (tt & 15)) * 4;
 
   for (int m0 = 0; m0 < M; m0 += 16 * GW_NT) {
     const int nt = min(GW_NT, (M - m0 + 15) / 16);  // uniform
-    int x_off[GW_NT], pa[GW_NT];
+    const int pt = P.route.perm()[pstart + min(m0 + tt, M - 1)];  // tokens past the last repeat it
+    if (q == 0) s_pair[tt] = pt;
+    const int x_off = (pt / P.top_k) * P.cols * 2 + 64 * q;
+    auto xload = [&](int sb, u32x4(&dst)[4]) {
 #pragma unroll
-    for (int ti = 0; ti < GW_NT; ti++) {
-      pa[ti] = P.route.perm()[pstart + min(m0 + 16 * ti + n, M - 1)];
-      x_off[ti] = (pa[ti] / P.top_k) * P.cols * 2 + 16 * g;
-    }
+      for (int i = 0; i < 4; i++)
+        dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, x_off + 16 * i, sb * 512, 0));
+    };
+    // Two superblocks in flight: register set k holds superblocks k, k + 2, ...
+    // (loads past the last superblock re-read it and are not used).
+    u32x4 v[2][4];
+    GwBuf W[2];
+    xload(0, v[0]);
+    gw_issue(st, 0, W[0]);
+    xload(min(1, nsb - 1), v[1]);
+    gw_issue(st, min(1, nsb - 1), W[1]);
     f32x4_t acc[GW_NT][2];
 #pragma unroll
     for (int ti = 0; ti < GW_NT; ti++) acc[ti][0] = acc[ti][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    GwBuf A, B;
-    gw_issue(st, 0, A);
-    for (int sb = 0;; sb += 2) {
-      gw_issue(st, min(sb + 1, nsb - 1), B);
-      __builtin_amdgcn_sched_barrier(0);
-      gw_compute(st, x_off, nt, sb, A, g, &lds_tab[0], &signs[0], acc);
-      if (sb + 1 >= nsb) break;
-      gw_issue(st, min(sb + 2, nsb - 1), A);
-      __builtin_amdgcn_sched_barrier(0);
-      gw_compute(st, x_off, nt, sb + 1, B, g, &lds_tab[0], &signs[0], acc);
-      if (sb + 2 >= nsb) break;
+    for (int sb = 0; sb < nsb; sb += 2) {
+#pragma unroll
+      for (int k = 0; k < 2; k++) {
+        if (sb + k < nsb) {  // uniform
+#pragma unroll
+          for (int i = 0; i < 4; i++) stg[k].x[sidx + i] = v[k][i];
+          xload(min(sb + k + 2, nsb - 1), v[k]);
+          __syncthreads();
+          gw_compute(nt, W[k], stg[k], n, g, &lds_tab[0], &signs[0], acc);
+          gw_issue(st, min(sb + k + 2, nsb - 1), W[k]);
+        }
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // pairs of tokens 16 ti + 4g + r from lane 4g + r, as in k_gu_iq2
-    int pr[GW_NT][4];
-#pragma unroll
-    for (int ti = 0; ti < GW_NT; ti++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) pr[ti][r] = __shfl(pa[ti], 4 * g + r, 64);
     if (n0 + n < P.rows) {
 #pragma unroll
       for (int ti = 0; ti < GW_NT; ti++)
 #pragma unroll
         for (int r = 0; r < 4; r++)
           if (ti < nt && m0 + 16 * ti + 4 * g + r < M)
-            P.out[(size_t)pr[ti][r] * P.rows + n0 + n] = silu_mul(acc[ti][0][r], acc[ti][1][r]);
+            P.out[(size_t)s_pair[16 * ti + 4 * g + r] * P.rows + n0 + n] = silu_mul(acc[ti][0][r], acc[ti][1][r]);
     }
+    __syncthreads();  // the staging buffers and s_pair are rewritten by the next pass
   }
 }
 
