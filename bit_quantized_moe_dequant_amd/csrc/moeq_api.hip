@@ -189,6 +189,12 @@ double pairs_per_expert(const moeq_layer* L, int T) {
 }
 bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >= MOEQ_GROUPED_WIDE_FROM; }
 
+// IQ2_XXS gate/up for T > 1: the two-tile kernel from this many pairs per expert
+// (T K / E), the one-tile kernel below it.
+#ifndef MOEQ_IQ2_WIDE_FROM
+#define MOEQ_IQ2_WIDE_FROM 8.0
+#endif
+
 // Q2_K down partials on the matrix instruction (decode once per 16 tokens) from
 // this many expected pairs per touched expert; below it most of a 16-token tile is
 // padding and the GEMV is faster (measured at 1.2 and 1.9 pairs: 415 vs 328 us and
@@ -212,7 +218,7 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
   if (L->gate.fmt == MOEQ_FMT_IQ2_XXS && gu_iq2_fits(L->inter, L->hidden))
-    return hip_rc(launch_gu_iq2(p, slots, (double)T * L->top_k >= 8.0 * L->n_experts, s));
+    return hip_rc(launch_gu_iq2(p, slots, (double)T * L->top_k >= MOEQ_IQ2_WIDE_FROM * L->n_experts, s));
   return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, grouped_wide(L, T) ? 4 : 1, s, ev));
 }
 
