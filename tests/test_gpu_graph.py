@@ -28,6 +28,8 @@ def say(*a):
     # (H, I, E, K, gate/up format, down format, T, calls per graph)
     (1024, 512, 16, 6, mq.FMT_MXFP4, mq.FMT_MXFP4, 1, 3),
     (1024, 512, 16, 6, mq.FMT_NVFP4, mq.FMT_Q2_K, 16, 2),
+    (1024, 512, 16, 6, mq.FMT_NVFP4, mq.FMT_MXFP4, 1, 3),   # NVFP4 gate/up on the matrix unit
+    (512, 256, 4, 2, mq.FMT_IQ2_XXS, mq.FMT_Q2_K, 32, 2),   # 16 pairs per expert: the two-tile IQ2_XXS gate/up and grouped Q2_K down
     (512, 256, 8, 2, mq.FMT_MXFP4, mq.FMT_MXFP4, 256, 2),   # prefill path (T >= 128, MXFP4)
 ])
 def test_graph_replays_match_eager(case):
