@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoeq.so")
 
-SOURCES = ["moeq_api.hip", "moeq_gemv.hip", "moeq_fused.hip", "moeq_aux.hip", "moeq_prefill.hip", "moeq_linear.hip", "moeq_grouped.hip", "moeq_gu_mx4.hip", "synth.hip"]
+SOURCES = ["moeq_api.hip", "moeq_gemv.hip", "moeq_aux.hip", "moeq_prefill.hip", "moeq_linear.hip", "moeq_grouped.hip", "moeq_gu_mx4.hip", "synth.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

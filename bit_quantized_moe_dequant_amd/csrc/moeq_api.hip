@@ -15,10 +15,6 @@ namespace {
 
 constexpr int PREFILL_MIN_T = 128;
 
-// The one-launch single-token layer (moeq_fused.hip) is correct but, as measured
-// on MI355X, slower than the gate/up + down launches; it stays off until it wins.
-constexpr bool kOneLaunchLayer = false;
-
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -146,8 +142,6 @@ int check_ws(const moeq_layer* L, int T, void* ws, size_t ws_bytes) {
 inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOEQ_OK : MOEQ_E_HIP; }
 inline hipStream_t S(void* s) { return (hipStream_t)s; }
 inline uint32_t* err_word(void* ws) { return (uint32_t*)ws; }
-// three queue counters of the one-launch layer, in their own 128-byte line
-inline uint32_t* counters(void* ws) { return (uint32_t*)((uint8_t*)ws + 128); }
 inline RouteView route_view(const moeq_layer* L, void* ws, const WsLayout& lay) {
   RouteView rv;
   rv.base = (int32_t*)((uint8_t*)ws + lay.route);
@@ -494,27 +488,6 @@ int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, 
     if ((rc = hip_rc(launch_quant_mxfp8(0, x, T, L->hidden, xq, xs, s)))) return rc;
     if ((rc = run_prefill_gate_up(L, xq, xs, T, nullptr, hq, hs, ws, lay, s))) return rc;
     return run_prefill_down(L, hq, hs, rw, T, y, ws, lay, s);
-  }
-  if (kOneLaunchLayer && T == 1 && fused1_supported(L->gate.fmt, L->down.fmt, L->hidden, L->inter, L->top_k)) {
-    FusedParams f;
-    memset(&f, 0, sizeof(f));
-    f.g[0] = ref_of(L->gate);
-    f.g[1] = ref_of(L->up);
-    f.d = ref_of(L->down);
-    f.grid_g = L->gate.grid;
-    f.grid_d = L->down.grid;
-    f.hidden = L->hidden;
-    f.inter = L->inter;
-    f.n_experts = L->n_experts;
-    f.top_k = L->top_k;
-    f.x = x;
-    f.ids = ids;
-    f.rw = rw;
-    f.h = h;
-    f.y = y;
-    f.err = err_word(ws);
-    f.counters = counters(ws);
-    return hip_rc(launch_fused1(L->gate.fmt, L->down.fmt, f, s));
   }
   if ((rc = run_gate_up(L, x, ids, T, h, ws, lay, s))) return rc;
   return run_down(L, h, ids, rw, T, y, ws, lay, s);

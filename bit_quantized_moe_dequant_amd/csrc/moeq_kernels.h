@@ -70,24 +70,7 @@ struct Down1Params {
 };
 
 // Device error word bits (mirrors MOEQ_DEVERR_* in moeq.h).
-constexpr uint32_t MOEQ_ERRBIT_EXPERT = 1u, MOEQ_ERRBIT_SPIN = 2u;
-
-struct FusedParams {
-  WeightRef g[2];   // gate, up
-  WeightRef d;      // down
-  const uint8_t* grid_g;
-  const uint8_t* grid_d;
-  int hidden, inter, n_experts, top_k;
-  int lpr_g, lpr_d, chunks_g, chunks_d, n_gu, n_dn;
-  const void* x;    // bf16 [hidden]
-  const int32_t* ids;
-  const float* rw;
-  float* h;         // fp32 [top_k][inter] (workspace)
-  float* y;         // fp32 [hidden]
-  uint32_t* err;
-  uint32_t* counters;  // 3 words in the workspace header, zero between launches
-  uint32_t spin_limit;
-};
+constexpr uint32_t MOEQ_ERRBIT_EXPERT = 1u;
 
 struct PrefillParams {
   WeightRef w[2];        // gate/up pass: gate, up; down pass: down (w[0])
@@ -128,8 +111,6 @@ hipError_t launch_quant_mxfp8(int in_f32, const void* x, int T, int K, uint8_t* 
 hipError_t launch_pack(int fmt, const uint8_t* blocks, int rows, int cols, int n, uint8_t* data, uint8_t* scales,
                        hipStream_t s);
 hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s);
-bool fused1_supported(int fg, int fd, int hidden, int inter, int top_k);
-hipError_t launch_fused1(int fg, int fd, const FusedParams& p, hipStream_t s);
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int n_slots, hipStream_t s);
 bool gu1_mx4_fits(int rows, int cols);  // cols % 512 == 0, cols <= 4096
 // Single-token gate/up + SwiGLU for MXFP4 or NVFP4 on the block-scaled matrix instruction.

@@ -102,7 +102,6 @@ extern "C" {
 
 /* Bits of the device error word (first 4 bytes of a workspace). */
 #define MOEQ_DEVERR_EXPERT_ID 1u /* an expert id was outside [0, n_experts) */
-#define MOEQ_DEVERR_SPIN 2u      /* a cross-work-group wait gave up (results invalid) */
 
 /* ------------------------------------------------------------------ descriptors
  * Read on the host only, during the call. */

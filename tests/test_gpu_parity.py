@@ -220,7 +220,7 @@ def test_forward_small_layers(case, T):
     assert rel_err(h.reshape(T, K, I), ref_h) < TOL
     assert rel_err(y, ref_y) < TOL
     assert rel_err(y2, ref_y) < TOL
-    assert rel_err(y, y2) < 1e-5          # one-launch layer vs the stage kernels
+    assert rel_err(y, y2) < 1e-5          # the layer call vs its stages called one by one
 
 
 @pytest.mark.parametrize("T,I", [(40, 224), (7, 64)])
@@ -303,10 +303,10 @@ def test_fp4_gate_up_scale_alignment(fmt):
     assert rel_err(h4.reshape(1, 3, 512), ref_h) < TOL
 
 
-def test_one_launch_layer_repeats_exactly():
-    """The single-token layer runs as one work-queue launch whose counters reset at
-    the end of each launch: many launches in a row must give identical results."""
-    say("one-launch repeats")
+def test_layer_repeats_exactly():
+    """Every sum runs in a fixed order (no float atomics, the combine walks the
+    slots in order), so fifty calls in a row on one workspace agree bit for bit."""
+    say("layer repeats")
     spec = workloads.LayerSpec(2048, 1024, 32, 6, 1, 1, seed=5)
     layer = upload_layer(spec)
     ids, rw = synth.uniform_routing(6, 1, 32, 6)
