@@ -64,27 +64,24 @@ __device__ __forceinline__ v16f mfma_fp8_fp4(const v8i& a, const v8i& b, const v
                                                          sb);
 }
 
-// E4M3FN round-to-nearest-even of v (saturating, sign kept); same rule as the
-// activation quantiser.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  uint32_t sign = (f2u(v) >> 24) & 0x80u;
-  float a = __builtin_fabsf(v);
-  uint32_t code;
-  if (!(a < 448.0f)) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    int e = (int)((f2u(a) >> 23) & 0xFFu) - 127;
-    uint32_t q = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));
-    if (q == 16u) {
-      e += 1;
-      q = 8u;
-    }
-    code = ((uint32_t)(e + 7) << 3) | (q - 8u);
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return code | sign;
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// E4M3FN codes of a and b, round to nearest even, saturating to 448 with the sign
+// kept (the activation quantiser's rule). The hardware conversion rounds to
+// nearest even and handles subnormals the same way; it differs only above 448,
+// where it gives NaN, and the select restores saturation there. Under the scale
+// that mx_exponent picks, finite inputs never exceed 448.
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  uint32_t w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, a, b, 1.0f, false));
+  if (!(__builtin_fabsf(a) <= 448.0f)) w = (w & 0xFF00u) | 0x7Eu | ((f2u(a) >> 24) & 0x80u);
+  if (!(__builtin_fabsf(b) <= 448.0f)) w = (w & 0x00FFu) | ((0x7Eu | ((f2u(b) >> 24) & 0x80u)) << 8);
+  return w;
+}
+
+// max of v and its partner under a lane permutation inside each 16-lane row
+template <int CTRL>
+__device__ __forceinline__ float max_dpp(float v) {
+  return __builtin_fmaxf(v, u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), CTRL, 0xF, 0xF, false)));
 }
 
 __device__ __forceinline__ uint32_t mx_exponent(float amax) {
@@ -401,29 +398,65 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
 
   // epilogue
   const int mt = two_tiles ? 2 : 1;
+  if constexpr (GATE_UP) {
+    // h = silu(g) u, then MXFP8 of each token row's 32 features of this tile. Row m's
+    // 32 values are register r of the 32 lanes of one half: their maximum comes from
+    // four in-row lane permutations (xor 1, xor 2, the 8-lane and the 16-lane
+    // mirror) and one exchange between the half's two 16-lane rows. Each step runs
+    // over all sixteen registers before the next, so the exchanges overlap.
+    const int xaddr = (lane ^ 16) << 2;
 #pragma unroll
-  for (int t = 0; t < 2; t++) {
-    if (t >= mt) continue;
+    for (int t = 0; t < 2; t++) {
+      if (t >= mt) continue;
+      float hv[16], am[16];
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int m = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * g;
-      const bool live = m < M;
-      const size_t pair = (size_t)pair_lds[m];
-      if (GATE_UP) {
-        const float hv = silu_mul(acc[0][t][r], acc[NS - 1][t][r]);
-        if (live && P.h_f32) P.h_f32[pair * P.rows + n0 + n] = hv;
-        // MXFP8 over this tile's 32 features of row m: the 32 lanes of one half hold the row
-        float amax = __builtin_fabsf(hv);
+      for (int r = 0; r < 16; r++) {
+        hv[r] = silu_mul(acc[0][t][r], acc[NS - 1][t][r]);
+        am[r] = __builtin_fabsf(hv[r]);
+      }
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
-        const uint32_t E = amax == 0.f ? 0u : mx_exponent(amax);
-        const uint32_t code = amax == 0.f ? 0u : e4m3_code(__builtin_ldexpf(hv, 127 - (int)E));
-        if (live) {
-          P.hq[pair * P.rows + n0 + n] = (uint8_t)code;
-          if (n == 0) P.hs[pair * (P.rows / 32) + n0 / 32] = (uint8_t)E;
+      for (int r = 0; r < 16; r++) am[r] = max_dpp<0xB1>(am[r]);   // quad_perm [1,0,3,2]
+#pragma unroll
+      for (int r = 0; r < 16; r++) am[r] = max_dpp<0x4E>(am[r]);   // quad_perm [2,3,0,1]
+#pragma unroll
+      for (int r = 0; r < 16; r++) am[r] = max_dpp<0x141>(am[r]);  // row_half_mirror
+#pragma unroll
+      for (int r = 0; r < 16; r++) am[r] = max_dpp<0x140>(am[r]);  // row_mirror
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        am[r] = __builtin_fmaxf(am[r], u2f((uint32_t)__builtin_amdgcn_ds_bpermute(xaddr, (int)f2u(am[r]))));
+      uint32_t E[16], code[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) E[r] = am[r] == 0.f ? 0u : mx_exponent(am[r]);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const uint32_t w = e4m3_pair(__builtin_ldexpf(hv[r], 127 - (int)E[r]),
+                                     __builtin_ldexpf(hv[r + 1], 127 - (int)E[r + 1]));
+        code[r] = am[r] == 0.f ? 0u : (w & 0xFFu);
+        code[r + 1] = am[r + 1] == 0.f ? 0u : ((w >> 8) & 0xFFu);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * g;
+        if (m < M) {
+          const size_t pair = (size_t)pair_lds[m];
+          if (P.h_f32) P.h_f32[pair * P.rows + n0 + n] = hv[r];
+          P.hq[pair * P.rows + n0 + n] = (uint8_t)code[r];
+          if (n == 0) P.hs[pair * (P.rows / 32) + n0 / 32] = (uint8_t)E[r];
         }
-      } else if (live) {
-        P.partial[pair * P.rows + n0 + n] = acc[0][t][r] * P.rw[pair];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      if (t >= mt) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * g;
+        if (m < M) {
+          const size_t pair = (size_t)pair_lds[m];
+          P.partial[pair * P.rows + n0 + n] = acc[0][t][r] * P.rw[pair];
+        }
       }
     }
   }
