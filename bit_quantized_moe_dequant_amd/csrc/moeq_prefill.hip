@@ -21,17 +21,17 @@
 // scale of K-block L/32; C lane L register r is row (r%4) + 8(r/4) + 4(L/32),
 // column L%32.
 //
-// Schedule. A work item is (64 pairs of one expert, 256 weight rows); the route
-// kernel lists the 64-pair chunks of every expert. Each of the eight waves owns 32
-// rows: for gate/up it streams the gate and the up rows of the same 32 features,
-// which share every A fragment it reads (half the LDS reads per matrix
-// instruction, and SwiGLU needs no exchange); for down one 32-row tile, which
-// leaves registers for two work-groups per compute unit. K advances in chunks of
-// 256 (eight 32-blocks): the chunk's A tile (64 token rows x 256 bytes, gathered
-// through the routing permutation) is staged once in LDS, double-buffered, and
-// shared by the eight waves; the weights go straight from HBM to registers one
-// chunk ahead. Items with at most 32 pairs skip the second token tile's
-// instructions.
+// Schedule. A work item is (64 pairs of one expert, a tile of weight rows); the
+// route kernel lists the 64-pair chunks of every expert. Each wave owns 32 rows:
+// for gate/up it streams the gate and the up rows of the same 32 features, which
+// share every A fragment it reads (half the LDS reads per matrix instruction, and
+// SwiGLU needs no exchange), four waves to a work-group; for down one 32-row tile,
+// eight waves to a work-group. Either way two work-groups share a compute unit.
+// K advances in chunks of 256 (eight 32-blocks): the chunk's A tile (64 token
+// rows x 256 bytes, gathered through the routing permutation) is staged once in
+// LDS, double-buffered, and shared by the group's waves; the weights go straight
+// from HBM to registers one chunk ahead. Items with at most 32 pairs skip the
+// second token tile's instructions.
 //
 // Order of K inside a chunk. The contraction is a sum, so any order of the eight
 // 32-blocks is the same product as long as A, B and both scales follow it. The
@@ -51,13 +51,14 @@ typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int PF_KC = 256;                 // K per chunk
-constexpr int PF_WAVES = 8;
-constexpr int PF_THREADS = 64 * PF_WAVES;
-constexpr int PF_PIECES = 1024 / PF_THREADS;  // 16-byte pieces of the A tile per thread
+// Waves per work-group: gate/up 4 (each wave needs about 240 registers, so two
+// work-groups share a compute unit and one's prologue and epilogue overlap the
+// other's weight stream), down 8 (128 registers: two 8-wave groups per unit).
+__host__ __device__ constexpr int pf_waves(bool gate_up) { return gate_up ? 4 : 8; }
 constexpr int PF_STRIDE = PF_KC + 16;      // LDS row of the A tile, padded by 16 bytes
 
 // weight rows per work-group: 32 per wave (gate/up: 32 features, gate and up rows)
-__host__ __device__ constexpr int pf_rows(bool) { return 32 * PF_WAVES; }
+__host__ __device__ constexpr int pf_rows(bool gate_up) { return 32 * pf_waves(gate_up); }
 
 __device__ __forceinline__ v16f mfma_fp8_fp4(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0, sa, 0,
@@ -119,14 +120,18 @@ constexpr int PF_SG = 4;
 constexpr int PF_SROW = 8 * PF_SG + 4;
 __host__ __device__ constexpr int pf_weight_tiles(bool gate_up) { return gate_up ? 2 : 1; }
 
-// down: 16 waves per compute unit (two work-groups), gate/up: what fits
+// two waves per SIMD for gate/up (two 4-wave groups per compute unit), four for
+// down (two 8-wave groups)
 template <bool GATE_UP>
-__global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE_UP ? 1 : 4))) void k_prefill(
+__global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((amdgpu_waves_per_eu(GATE_UP ? 2 : 4))) void k_prefill(
     PrefillParams P) {
   // weight tiles per wave: gate/up two (gate and up rows of the same features),
   // down one
   constexpr int NS = pf_weight_tiles(GATE_UP);
   constexpr int ROWS = pf_rows(GATE_UP);
+  constexpr int PF_THREADS = 64 * pf_waves(GATE_UP);
+  constexpr int PF_PIECES = 1024 / PF_THREADS;  // 16-byte pieces of the A tile per thread
+  static_assert(PF_THREADS >= 256, "one A-scale piece (64 rows x 4 chunks) per thread");
   constexpr int NBP = NS * ROWS * PF_SG / PF_THREADS;  // weight-scale pieces per thread per group
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][PREFILL_MC][PF_STRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t bs_ring[2][NS * ROWS][PF_SROW];
@@ -464,7 +469,8 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(GATE
 
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int /*n_slots*/, hipStream_t s) {
   // rows and cols are multiples of 256 (checked by the caller)
-  dim3 g((unsigned)(p.rows / pf_rows(gate_up)), (unsigned)RouteView::max_chunks(p.route.E, p.route.P)), b(PF_THREADS);
+  dim3 g((unsigned)(p.rows / pf_rows(gate_up)), (unsigned)RouteView::max_chunks(p.route.E, p.route.P)),
+      b((unsigned)(64 * pf_waves(gate_up)));
   if (gate_up) hipLaunchKernelGGL(k_prefill<true>, g, b, 0, s, p);
   else hipLaunchKernelGGL(k_prefill<false>, g, b, 0, s, p);
   return hipGetLastError();
