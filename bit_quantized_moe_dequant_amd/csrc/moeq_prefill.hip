@@ -25,8 +25,8 @@
 // route kernel lists the 64-pair chunks of every expert. Each wave owns 32 rows:
 // for gate/up it streams the gate and the up rows of the same 32 features, which
 // share every A fragment it reads (half the LDS reads per matrix instruction, and
-// SwiGLU needs no exchange), four waves to a work-group; for down one 32-row tile,
-// eight waves to a work-group. Either way two work-groups share a compute unit.
+// SwiGLU needs no exchange); for down one 32-row tile. Four waves make a
+// work-group, two (gate/up) or three (down) of which share a compute unit.
 // K advances in chunks of 256 (eight 32-blocks): the chunk's A tile (64 token
 // rows x 256 bytes, gathered through the routing permutation) is staged once in
 // LDS, double-buffered, and shared by the group's waves; the weights go straight
@@ -51,10 +51,13 @@ typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int PF_KC = 256;                 // K per chunk
-// Waves per work-group: gate/up 4 (each wave needs about 240 registers, so two
-// work-groups share a compute unit and one's prologue and epilogue overlap the
-// other's weight stream), down 8 (128 registers: two 8-wave groups per unit).
-__host__ __device__ constexpr int pf_waves(bool gate_up) { return gate_up ? 4 : 8; }
+// Waves per work-group: 4. Gate/up waves need about 250 registers, so two groups
+// share a compute unit; down waves get up to 168, three groups to a unit (at 128
+// the compiler spills loop-invariant addresses, and every reload waits for the
+// whole load queue). Several independent groups per unit let one's prologue and
+// epilogue overlap the others' weight streams.
+__host__ __device__ constexpr int pf_waves(bool) { return 4; }
+__host__ __device__ constexpr int pf_waves_per_simd(bool gate_up) { return gate_up ? 2 : 3; }
 constexpr int PF_STRIDE = PF_KC + 16;      // LDS row of the A tile, padded by 16 bytes
 
 // weight rows per work-group: 32 per wave (gate/up: 32 features, gate and up rows)
@@ -120,10 +123,9 @@ constexpr int PF_SG = 4;
 constexpr int PF_SROW = 8 * PF_SG + 4;
 __host__ __device__ constexpr int pf_weight_tiles(bool gate_up) { return gate_up ? 2 : 1; }
 
-// two waves per SIMD for gate/up (two 4-wave groups per compute unit), four for
-// down (two 8-wave groups)
 template <bool GATE_UP>
-__global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((amdgpu_waves_per_eu(GATE_UP ? 2 : 4))) void k_prefill(
+__global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((
+    amdgpu_waves_per_eu(pf_waves_per_simd(GATE_UP)))) void k_prefill(
     PrefillParams P) {
   // weight tiles per wave: gate/up two (gate and up rows of the same features),
   // down one
@@ -137,6 +139,7 @@ __global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((amdgpu_waves
   __shared__ __attribute__((aligned(16))) uint8_t bs_ring[2][NS * ROWS][PF_SROW];
   __shared__ __attribute__((aligned(16))) uint8_t as_ring[2][PREFILL_MC][PF_SROW];
   __shared__ int pair_lds[PREFILL_MC];
+  __shared__ float rw_lds[PREFILL_MC];  // down: route weight of each pair of the item
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,6 +168,12 @@ __global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((amdgpu_waves
     return;
   }
 
+  // down: thread tid < 64 fetches pair tid's route weight now and publishes it in
+  // LDS only at the epilogue, so the load's latency hides behind the K loop
+  float rw_mine = 0.f;
+  if constexpr (!GATE_UP) {
+    if (tid < PREFILL_MC) rw_mine = P.rw[pair_lds[tid]];
+  }
   const int n = lane & 31, g = lane >> 5;
   const int nchunks = P.cols / PF_KC;
   const bool two_tiles = M > 32;
@@ -408,15 +417,25 @@ __global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((amdgpu_waves
     // 32 values are register r of the 32 lanes of one half: their maximum comes from
     // four in-row lane permutations (xor 1, xor 2, the 8-lane and the 16-lane
     // mirror) and one exchange between the half's two 16-lane rows. Each step runs
-    // over all sixteen registers before the next, so the exchanges overlap.
+    // over all sixteen registers before the next, so the exchanges overlap. The
+    // codes go out through raw buffer stores with 32-bit offsets (hq and hs hold
+    // fewer than 2^31 bytes, checked by the caller); a row past the item's last
+    // pair gets an offset past the buffer's range, which the hardware drops.
     const int xaddr = (lane ^ 16) << 2;
+    const __amdgpu_buffer_rsrc_t hq_buf = raw_buffer(P.hq), hs_buf = raw_buffer(P.hs);
+    constexpr uint32_t kDrop = 0x7FFFFFFFu;  // the descriptors' record count
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       if (t >= mt) continue;
       float hv[16], am[16];
+      int pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) pr[r] = pair_lds[32 * t + (r & 3) + 8 * (r >> 2) + 4 * g];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        hv[r] = silu_mul(acc[0][t][r], acc[NS - 1][t][r]);
+        // silu(g) u with the hardware reciprocal (about 1 ulp)
+        const float gv = acc[0][t][r];
+        hv[r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[NS - 1][t][r];
         am[r] = __builtin_fabsf(hv[r]);
       }
 #pragma unroll
@@ -442,26 +461,37 @@ __global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((amdgpu_waves
       }
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int m = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * g;
-        if (m < M) {
-          const size_t pair = (size_t)pair_lds[m];
-          if (P.h_f32) P.h_f32[pair * P.rows + n0 + n] = hv[r];
-          P.hq[pair * P.rows + n0 + n] = (uint8_t)code[r];
-          if (n == 0) P.hs[pair * (P.rows / 32) + n0 / 32] = (uint8_t)E[r];
-        }
+        const bool live = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * g < M;
+        const uint32_t row = (uint32_t)pr[r];
+        const uint32_t oq = live ? row * (uint32_t)P.rows + (uint32_t)(n0 + n) : kDrop;
+        const uint32_t os = live && n == 0 ? row * (uint32_t)(P.rows / 32) + (uint32_t)(n0 / 32) : kDrop;
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code[r], hq_buf, oq, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)E[r], hs_buf, os, 0, 0);
+      }
+      if (P.h_f32) {
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if (32 * t + (r & 3) + 8 * (r >> 2) + 4 * g < M) P.h_f32[(size_t)pr[r] * P.rows + n0 + n] = hv[r];
       }
     }
   } else {
+    if (tid < PREFILL_MC) rw_lds[tid] = rw_mine;
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       if (t >= mt) continue;
+      int pr[16];
+      float w[16];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int m = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * g;
-        if (m < M) {
-          const size_t pair = (size_t)pair_lds[m];
-          P.partial[pair * P.rows + n0 + n] = acc[0][t][r] * P.rw[pair];
-        }
+        pr[r] = pair_lds[m];
+        w[r] = rw_lds[m];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        if (32 * t + (r & 3) + 8 * (r >> 2) + 4 * g < M)
+          P.partial[(size_t)pr[r] * P.rows + n0 + n] = acc[0][t][r] * w[r];
       }
     }
   }
