@@ -424,6 +424,8 @@ __device__ __forceinline__ void gq_stage_write(const u32x4 (&v)[4], int tm, int 
 __device__ __forceinline__ void gq_compute(const GqW& b, const GqStage& s, int n, int g, f32x4_t& acc) {
   const uint32_t ONE = 0x3F803F80u;
   const float d = half_bits_f32(b.dd), dmin = half_bits_f32(b.dd >> 16);
+  // d F for the four crumb positions (F = 128, 32, 8, 4: exact powers of two)
+  const float dF[4] = {d * 128.f, d * 32.f, d * 8.f, d * 4.f};
 #pragma unroll
   for (int c = 0; c < 4; c++) {
     const uint32_t w = b.w[c], w8 = b.w[c] >> 8;
@@ -447,11 +449,12 @@ __device__ __forceinline__ void gq_compute(const GqW& b, const GqStage& s, int n
       cq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gq_pair(av[2], av[3]), bv, cq, 0, 0, 0);
       const f32x4_t hs = *reinterpret_cast<const f32x4_t*>(&s.h[j * 16 + 4 * g]);  // tokens 4g .. 4g + 3
       const uint32_t byte = (b.sc[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-      constexpr float F[4] = {128.f, 32.f, 8.f, 4.f};
-      const float cs = d * F[p] * (float)(byte & 15u);  // d sc F: exact (11 x 4 bits, power of two)
-      const float cm = dmin * (float)(byte >> 4);       // exact
+      const float cs = dF[p] * (float)(byte & 15u);  // d sc F: exact (11 x 4 bits, power of two)
+      const float cm = dmin * (float)(byte >> 4);    // exact
+      // cs (cq - hs) - cm hs = cs cq - (cs + cm) hs
+      const float csm = cs + cm;
 #pragma unroll
-      for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(cs, cq[r] - hs[r], __builtin_fmaf(-cm, hs[r], acc[r]));
+      for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(-csm, hs[r], __builtin_fmaf(cs, cq[r], acc[r]));
     }
   }
 }
