@@ -192,12 +192,13 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
 
 // ---------------------------------------------------------------- many tokens per expert
 // Prefill-sized batches: each sub-block is decoded once and applied to GW_NT
-// 16-token tiles per pass, so the decode is shared by up to 16 GW_NT tokens
-// instead of 16. The pass's activations are staged once per superblock in LDS for
+// 16-token tiles per pass, so the decode is shared by up to 16 GW_NT = 64 tokens
+// instead of 16 (an expert with up to 64 pairs is decoded once). The pass's activations are staged once per superblock in LDS for
 // the work-group's four waves (each wave reading its own copy from L2 had been
 // half the kernel's time), in two buffers with one barrier per superblock, and the
 // activation and weight loads run two superblocks ahead.
-constexpr int GW_NT = 2;
+constexpr int GW_NT = 4;
+constexpr int GW_RND = GW_NT / 2;  // staging rounds: 256 threads stage 32 tokens x 8 sub-blocks each
 
 struct GwBuf {
   u32x4 w[2][4];
@@ -302,24 +303,33 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
   st.x = gi_buffer(P.act);
   st.w_off = rn * nsb * 64;
   st.s_off = rn * nsb * 2;
-  // staging: thread = (pass token tt, sub-block q); its 64 bytes are the four
-  // 8-value groups of that sub-block
+  // staging: in round u, thread = (pass token tt + 32 u, sub-block q); its 64
+  // bytes are the four 8-value groups of that sub-block
+  static_assert(64 * GI_WAVES == 256 && GW_NT % 2 == 0, "staging covers 32 tokens per round");
   const int tt = threadIdx.x >> 3, q = threadIdx.x & 7;
-  const int sidx = (((tt >> 4) * 8 + q) * 16 + (tt & 15)) * 4;
 
   for (int m0 = 0; m0 < M; m0 += 16 * GW_NT) {
     const int nt = min(GW_NT, (M - m0 + 15) / 16);  // uniform
-    const int pt = P.route.perm()[pstart + min(m0 + tt, M - 1)];  // tokens past the last repeat it
-    if (q == 0) s_pair[tt] = pt;
-    const int x_off = (pt / P.top_k) * P.cols * 2 + 64 * q;
-    auto xload = [&](int sb, u32x4(&dst)[4]) {
+    int x_off[GW_RND], sidx[GW_RND];
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, x_off + 16 * i, sb * 512, 0));
+    for (int u = 0; u < GW_RND; u++) {
+      const int tk = tt + 32 * u;
+      const int pt = P.route.perm()[pstart + min(m0 + tk, M - 1)];  // tokens past the last repeat it
+      if (q == 0) s_pair[tk] = pt;
+      x_off[u] = (pt / P.top_k) * P.cols * 2 + 64 * q;
+      sidx[u] = (((tk >> 4) * 8 + q) * 16 + (tk & 15)) * 4;
+    }
+    auto xload = [&](int sb, u32x4(&dst)[GW_RND][4]) {
+#pragma unroll
+      for (int u = 0; u < GW_RND; u++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          dst[u][i] =
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, x_off[u] + 16 * i, sb * 512, 0));
     };
     // Two superblocks in flight: register set k holds superblocks k, k + 2, ...
     // (loads past the last superblock re-read it and are not used).
-    u32x4 v[2][4];
+    u32x4 v[2][GW_RND][4];
     GwBuf W[2];
     xload(0, v[0]);
     gw_issue(st, 0, W[0]);
@@ -333,7 +343,9 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
       for (int k = 0; k < 2; k++) {
         if (sb + k < nsb) {  // uniform
 #pragma unroll
-          for (int i = 0; i < 4; i++) stg[k].x[sidx + i] = v[k][i];
+          for (int u = 0; u < GW_RND; u++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) stg[k].x[sidx[u] + i] = v[k][u][i];
           xload(min(sb + k + 2, nsb - 1), v[k]);
           __syncthreads();
           gw_compute(nt, W[k], stg[k], n, g, &lds_tab[0], &signs[0], acc);

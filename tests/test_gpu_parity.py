@@ -223,10 +223,12 @@ def test_forward_small_layers(case, T):
     assert rel_err(y, y2) < 1e-5          # the layer call vs its stages called one by one
 
 
-@pytest.mark.parametrize("T,I", [(40, 224), (7, 64)])
+@pytest.mark.parametrize("T,I", [(40, 224), (7, 64), (64, 128), (65, 96)])
 def test_iq2_grouped_gate_up(T, I):
     """IQ2_XXS gate/up for T > 1 (the matrix-instruction path): with two experts and
-    top-2 every expert gets all T tokens, so T = 40 spans three 16-token tiles;
+    top-2 every expert gets all T tokens (one fewer for the expert that loses the
+    out-of-range id), so T = 40 spans three 16-token tiles of one pass, T = 64 gives
+    passes of exactly 64 and 63 tokens and T = 65 a second pass of one token;
     I = 224 leaves the last 64-row work-group half empty; one out-of-range id puts
     a pair in the invalid bucket, whose h must be zero."""
     say("iq2 grouped", T, I)
