@@ -173,14 +173,17 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
       for (int j = 0; j < 16; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));  // the block's other half
       const uint32_t E = gu_mx_exponent(amax);
-      const int sh = 127 - (int)E;  // x / 2^(E - 127) is at most 448: no clipping
+      // The conversions take the block scale 2^(E - 127) as their scale operand
+      // (only its exponent field is read, as an e8m0 code): encoding divides by
+      // it, decoding multiplies by it, bit for bit as scaling by ldexp around
+      // unscaled conversions. x / 2^(E - 127) is at most 448: no clipping.
+      const float scale = u2f(E << 23);
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
-            i16x2_t{0, 0}, __builtin_ldexpf(x[4 * j], sh), __builtin_ldexpf(x[4 * j + 1], sh), 1.0f, false);
-        const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
-            lo, __builtin_ldexpf(x[4 * j + 2], sh), __builtin_ldexpf(x[4 * j + 3], sh), 1.0f, true);
+        const i16x2_t lo =
+            __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[4 * j], x[4 * j + 1], scale, false);
+        const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[4 * j + 2], x[4 * j + 3], scale, true);
         w[j] = (amax == 0.f) ? 0u : __builtin_bit_cast(uint32_t, hi);
       }
       *reinterpret_cast<u32x4*>(&st.code[term][k0]) = u32x4{w[0], w[1], w[2], w[3]};
@@ -189,12 +192,12 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
         // residual x - hi, exact in fp32
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, false);
-          const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, true);
-          x[4 * j] -= __builtin_ldexpf(a[0], -sh);
-          x[4 * j + 1] -= __builtin_ldexpf(a[1], -sh);
-          x[4 * j + 2] -= __builtin_ldexpf(b[0], -sh);
-          x[4 * j + 3] -= __builtin_ldexpf(b[1], -sh);
+          const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], scale, false);
+          const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], scale, true);
+          x[4 * j] -= a[0];
+          x[4 * j + 1] -= a[1];
+          x[4 * j + 2] -= b[0];
+          x[4 * j + 3] -= b[1];
         }
       }
     }
@@ -369,14 +372,13 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
       for (int j = 0; j < 16; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));  // the block's other half
       const uint32_t E = gu_mx_exponent(amax);
-      const int sh = 127 - (int)E;
+      const float scale = u2f(E << 23);  // the block scale as the conversions' scale operand
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
-            i16x2_t{0, 0}, __builtin_ldexpf(x[4 * j], sh), __builtin_ldexpf(x[4 * j + 1], sh), 1.0f, false);
-        const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
-            lo, __builtin_ldexpf(x[4 * j + 2], sh), __builtin_ldexpf(x[4 * j + 3], sh), 1.0f, true);
+        const i16x2_t lo =
+            __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[4 * j], x[4 * j + 1], scale, false);
+        const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[4 * j + 2], x[4 * j + 3], scale, true);
         w[j] = (amax == 0.f) ? 0u : __builtin_bit_cast(uint32_t, hi);
       }
       *reinterpret_cast<u32x4*>(&st.code[term][v]) = u32x4{w[0], w[1], w[2], w[3]};
@@ -384,12 +386,12 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
       if (term + 1 < DM_TERMS) {
 #pragma unroll
         for (int j = 0; j < 4; j++) {  // residual, exact in fp32
-          const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, false);
-          const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, true);
-          x[4 * j] -= __builtin_ldexpf(a[0], -sh);
-          x[4 * j + 1] -= __builtin_ldexpf(a[1], -sh);
-          x[4 * j + 2] -= __builtin_ldexpf(b[0], -sh);
-          x[4 * j + 3] -= __builtin_ldexpf(b[1], -sh);
+          const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], scale, false);
+          const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], scale, true);
+          x[4 * j] -= a[0];
+          x[4 * j + 1] -= a[1];
+          x[4 * j + 2] -= b[0];
+          x[4 * j + 3] -= b[1];
         }
       }
     }
