@@ -441,6 +441,23 @@ __device__ __forceinline__ void iq2_fill_lds(Iq2Lds* t, const uint8_t* grid, int
     t->grid[i] = (f32_bf16_rne((float)g0)) | (f32_bf16_rne((float)g1) << 16);
   }
 }
+// The same table in two halves, for a 256-thread work-group that should not wait
+// for the codebook before issuing its other loads: thread tid loads codebook entry
+// tid (8 bytes) first, and stores it once those loads are in flight.
+struct Iq2Entry {
+  uint32_t b[8];
+};
+__device__ __forceinline__ Iq2Entry iq2_load_entry(const uint8_t* grid, int tid) {
+  Iq2Entry e;
+#pragma unroll
+  for (int j = 0; j < 8; j++) e.b[j] = grid[8 * tid + j];
+  return e;
+}
+__device__ __forceinline__ void iq2_store_entry(Iq2Lds* t, const Iq2Entry& e, int tid) {
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+    t->grid[4 * tid + k] = f32_bf16_rne((float)e.b[2 * k]) | (f32_bf16_rne((float)e.b[2 * k + 1]) << 16);
+}
 
 // The four bf16-pair sign masks of one IQ2_XXS group from its 7-bit sign code c:
 // the 8-bit mask m is c plus its parity bit (an even number of negatives); word k

@@ -106,10 +106,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOEQ_GEMV_W
     return;
   }
 
-  if constexpr (FMT == FMT_IQ2_XXS) {
-    iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 256);
-    __syncthreads();
-  }
+  // IQ2_XXS codebook: each thread's entry is requested before the activation and
+  // weight loads and stored to LDS once they are in flight (first tile only), so
+  // the weight stream does not wait for it.
+  Iq2Entry gent;
+  if constexpr (FMT == FMT_IQ2_XXS) gent = iq2_load_entry(P.grid, threadIdx.x);
 
   WView W[NMAT];
 #pragma unroll
@@ -159,6 +160,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOEQ_GEMV_W
           }
         }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FMT == FMT_IQ2_XXS) {
+      if (m0 == 0) {  // uniform
+        iq2_store_entry(&lds_tab[0], gent, threadIdx.x);
+        __syncthreads();
+      }
+    }
     uint32_t x[MT][CPL][XN];
     float xs[MT][CPL][XS];
 #pragma unroll
