@@ -441,19 +441,28 @@ template <int FMT> struct GemvRows {
   static_assert(UB * NB == GEMV_UB * GEMV_NB, "rows per wave must not depend on the format");
 };
 
+// Token tile of the wide (several pairs per expert) launches. Every token of the
+// tile keeps its activation slices in registers for all of a lane's chunks, so the
+// tile shrinks as the chunks per lane grow: gate/up 4 tokens at one chunk per
+// lane, 2 at two (K = 4096 in FP4: a 4-token tile spilled about 100 registers and
+// an NVFP4 + Q2_K layer at T = 256 took 4.79 ms against 3.06 ms with 2-token
+// tiles), 1 at four; down and plain 2 and 4 tokens at one chunk per lane only
+// (their wider tiles spill hundreds of registers at two or more).
 template <int FMT, int CPL>
 static hipError_t gemv_fc(int epi, const GemvParams& p, dim3 g, int mt, hipStream_t s, const LaunchEvents* ev) {
   dim3 b(256);
   constexpr int UB = GemvRows<FMT>::UB, NB = GemvRows<FMT>::NB;
+  const bool wide = mt != 1;
   if (epi == EPI_SWIGLU) {
-    if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
-    else MOEQ_LAUNCH((k_gemv<FMT, CPL, 4, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
+    if (!wide || CPL >= 4) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
+    else if (CPL == 2) MOEQ_LAUNCH((k_gemv<FMT, CPL, 2, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
+    else MOEQ_LAUNCH((k_gemv<FMT, 1, 4, 2, EPI_SWIGLU, ACT_BF16, UB, NB>), g, b, s, ev, p);
   } else if (epi == EPI_PARTIAL) {
-    if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
-    else MOEQ_LAUNCH((k_gemv<FMT, CPL, 2, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
+    if (!wide || CPL >= 2) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
+    else MOEQ_LAUNCH((k_gemv<FMT, 1, 2, 1, EPI_PARTIAL, ACT_F32, UB, NB>), g, b, s, ev, p);
   } else {
-    if (mt == 1) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
-    else MOEQ_LAUNCH((k_gemv<FMT, CPL, 4, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
+    if (!wide || CPL >= 2) MOEQ_LAUNCH((k_gemv<FMT, CPL, 1, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
+    else MOEQ_LAUNCH((k_gemv<FMT, 1, 4, 1, EPI_PLAIN, ACT_BF16, UB, NB>), g, b, s, ev, p);
   }
   return hipGetLastError();
 }

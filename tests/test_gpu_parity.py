@@ -195,6 +195,8 @@ SMALL = [
     (2, 3, 2048, 1024, 4, 2),   # NVFP4 gate/up + Q2_K down, intermediate 1024
     (2, 1, 1536, 288, 4, 2),    # bs=1 NVFP4 gate/up on the matrix unit: the fourth wave gets no K step
     (2, 1, 512, 128, 3, 2),     # ... and a single wave of K steps
+    (2, 3, 4096, 256, 4, 2),    # K = 4096 in NVFP4: two chunks per lane; at T = 16 the 2-token gate/up tiles
+    (1, 1, 4096, 256, 4, 2),    # ... and in MXFP4
 ]
 
 
