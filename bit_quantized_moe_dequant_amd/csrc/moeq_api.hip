@@ -183,7 +183,8 @@ double pairs_per_expert(const moeq_layer* L, int T) {
 }
 bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >= MOEQ_GROUPED_WIDE_FROM; }
 
-// IQ2_XXS gate/up for T > 1: the two-tile kernel from this many pairs per expert
+// IQ2_XXS gate/up for T > 1: the wide kernel (up to four 16-token tiles per decode)
+// from this many pairs per expert
 // (T K / E), the one-tile kernel below it.
 #ifndef MOEQ_IQ2_WIDE_FROM
 #define MOEQ_IQ2_WIDE_FROM 8.0
@@ -192,9 +193,12 @@ bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >=
 // Q2_K down partials on the matrix instruction (decode once per 16 tokens) from
 // this many expected pairs per touched expert; below it most of a 16-token tile is
 // padding and the GEMV is faster (measured at 1.2 and 1.9 pairs: 415 vs 328 us and
-// 1199 vs 1159 us per layer; at 48 pairs the down took 4.5 ms against 11.3 ms).
+// 1199 vs 1159 us per layer). Above it the grouped kernel wins: at 3 and 6 pairs
+// (T = 128, 256 over 256 experts) the NVFP4 + Q2_K layer took 1415 and 1926 us
+// against 1845 and 3026 us with the GEMV; at 48 pairs the down took 4.5 ms against
+// 11.3 ms.
 #ifndef MOEQ_DN_Q2K_FROM
-#define MOEQ_DN_Q2K_FROM 8.0
+#define MOEQ_DN_Q2K_FROM 2.5
 #endif
 
 int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
