@@ -20,7 +20,7 @@
 namespace moeq {
 
 enum { FMT_MXFP4 = 1, FMT_NVFP4 = 2, FMT_Q2_K = 3, FMT_IQ2_XXS = 4, FMT_FP8_B128 = 5 };
-enum { ACT_BF16 = 0, ACT_F32 = 1, ACT_F32_COHERENT = 2 };
+enum { ACT_BF16 = 0, ACT_F32 = 1 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -66,18 +66,6 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// Four fp32 values read with agent-scope loads: coherent across the XCDs' L2s
-// (never a stale L2 copy), for data another work-group has just published.
-__device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-  u32x4 v;
-  v[0] = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v[1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v[2] = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v[3] = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
-}
 
 // -------------------------------------------------------------------------
 // Activation slices. XR<ACT>(n) = registers for n weights.
@@ -134,28 +122,6 @@ template <> struct Act<ACT_F32> {
       split_pair(u2f(v[i][0]), u2f(v[i][1]), r[2 * i], r[N / 2 + 2 * i]);
       split_pair(u2f(v[i][2]), u2f(v[i][3]), r[2 * i + 1], r[N / 2 + 2 * i + 1]);
     }
-  }
-  template <int N>
-  __device__ static void load(const void* row, int k0, uint32_t* r) {
-    u32x4 v[N / 4];
-    fetch<N>(row, k0, v);
-    from_raw<N>(v, r);
-  }
-  __device__ static float val(const void* row, int k) { return reinterpret_cast<const float*>(row)[k]; }
-};
-
-template <> struct Act<ACT_F32_COHERENT> {
-  static constexpr int PER_PAIR = 2;
-  // n contiguous fp32 values -> n/2 hi pairs then n/2 lo pairs
-  template <int N>
-  __device__ static void fetch(const void* row, int k0, u32x4* v) {
-    const float* p = reinterpret_cast<const float*>(row) + k0;
-#pragma unroll
-    for (int i = 0; i < N / 4; i++) v[i] = ld16_coherent(p + 4 * i);
-  }
-  template <int N>
-  __device__ static void from_raw(const u32x4* v, uint32_t* r) {
-    Act<ACT_F32>::template from_raw<N>(v, r);
   }
   template <int N>
   __device__ static void load(const void* row, int k0, uint32_t* r) {

@@ -69,8 +69,6 @@ struct Down1Params {
   int rows_per_wg, U;
 };
 
-// Device error word bits (mirrors MOEQ_DEVERR_* in moeq.h).
-constexpr uint32_t MOEQ_ERRBIT_EXPERT = 1u;
 
 struct PrefillParams {
   WeightRef w[2];        // gate/up pass: gate, up; down pass: down (w[0])
