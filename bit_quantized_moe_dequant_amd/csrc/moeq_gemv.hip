@@ -57,8 +57,16 @@ __global__ __launch_bounds__(256) void k_dequant(WeightRef w, const uint8_t* gri
 #ifndef MOEQ_GEMV_WPE
 #define MOEQ_GEMV_WPE 2  // waves per SIMD the register budget must allow
 #endif
+// Waves per SIMD the register budget must allow: MOEQ_GEMV_WPE, and one more for
+// the one-token Q2_K down partials, which stay unspilled at that budget and run
+// 4-6% faster with it (NVFP4 + Q2_K at T = 16, IQ2_XXS + Q2_K at T = 64); every
+// other variant measured slower or spilled at three.
+__host__ __device__ constexpr int gemv_wpe(int fmt, int epi, int mt) {
+  return (fmt == FMT_Q2_K && epi == EPI_PARTIAL && mt == 1) ? MOEQ_GEMV_WPE + 1 : MOEQ_GEMV_WPE;
+}
+
 template <int FMT, int CPL, int MT, int NMAT, int EPI, int ACT, int UB, int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOEQ_GEMV_WPE))) void k_gemv(GemvParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gemv_wpe(FMT, EPI, MT)))) void k_gemv(GemvParams P) {
   using D = Dec<FMT>;
   typedef typename D::Side Side;
   constexpr int XN = XRegs<FMT, ACT>::N;
