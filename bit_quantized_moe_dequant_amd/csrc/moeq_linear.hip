@@ -31,7 +31,11 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int LN_WAVES = 16;
+#ifndef MOEQ_LN_WAVES
+#define MOEQ_LN_WAVES 16
+#endif
+constexpr int LN_WAVES = MOEQ_LN_WAVES;
+static_assert(LN_WAVES % 4 == 0 && LN_WAVES <= 16, "whole 256-thread groups");
 constexpr int LN_THREADS = 64 * LN_WAVES;
 constexpr int LN_ROWS = 16;    // weight rows per work-group
 constexpr int LN_KSTEP = 256;  // K per step (two 128-wide scale tiles)
@@ -110,8 +114,9 @@ __global__ __launch_bounds__(LN_THREADS) void k_linear_fp8(LinearParams P) {
 #pragma unroll
       for (int r = 0; r < 4; r++) red[wave][ti][lr * 16 + 4 * g + r] = acc[ti][r];
     __syncthreads();
-    {
-      const int ti = threadIdx.x >> 8;
+    // 256 sums per token tile, one per thread (several tiles per thread when the
+    // work-group has fewer than 256 LN_TG threads)
+    for (int ti = (int)threadIdx.x >> 8; ti < LN_TG; ti += LN_THREADS / 256) {
       const int idx = threadIdx.x & 255;
       const int tok = ((tg + ti) << 4) + (idx >> 4);
       if (tg + ti < ntiles && tok < P.T) {
