@@ -13,18 +13,30 @@ namespace moeq {
 constexpr int ROUTE_MAX_E = 1024;
 
 __device__ int block_exclusive_scan(int v, int* tmp) {
-  // Hillis-Steele over blockDim.x (<= 1024) values; returns the exclusive prefix.
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-    int a = (t >= off) ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += a;
-    __syncthreads();
+  // Exclusive prefix over blockDim.x (a multiple of 64, <= 1024) values: an
+  // inclusive scan inside each wave by lane shuffles, then wave 0 scans the wave
+  // totals; three barriers in all. tmp holds at least 128 ints.
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  int incl = tmp[t];
+  if (lane == 63) tmp[w] = x;
   __syncthreads();
+  if (t < 64) {
+    int s = t < (int)(blockDim.x >> 6) ? tmp[t] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(s, off, 64);
+      if (t >= off) s += y;
+    }
+    tmp[64 + t] = s;  // inclusive prefix of the wave totals
+  }
+  __syncthreads();
+  const int incl = (w > 0 ? tmp[64 + w - 1] : 0) + x;
+  __syncthreads();  // tmp is reused by the next scan
   return incl - v;
 }
 
