@@ -48,14 +48,27 @@ __global__ __launch_bounds__(1024) void k_route(const int32_t* ids, int P, int E
   const int t = threadIdx.x;
   for (int i = t; i <= E; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
+  // Both passes over the ids read eight per thread before using any, so the
+  // loads overlap instead of each waiting a memory round trip.
+  constexpr int RB = 8;
   bool any_bad = false;
-  for (int p = t; p < P; p += blockDim.x) {
-    int e = ids[p];
-    if (e < 0 || e >= E) {
-      e = E;
-      any_bad = true;
+  for (int p0 = t; p0 < P; p0 += RB * (int)blockDim.x) {
+    int ev[RB];
+#pragma unroll
+    for (int j = 0; j < RB; j++) {
+      const int p = p0 + j * (int)blockDim.x;
+      ev[j] = p < P ? ids[p] : 0;
     }
-    atomicAdd(&cnt[e], 1);
+#pragma unroll
+    for (int j = 0; j < RB; j++) {
+      if (p0 + j * (int)blockDim.x >= P) break;
+      int e = ev[j];
+      if (e < 0 || e >= E) {
+        e = E;
+        any_bad = true;
+      }
+      atomicAdd(&cnt[e], 1);
+    }
   }
   if (any_bad) atomicOr(err, 1u);  // expert id out of range
   __syncthreads();
@@ -96,11 +109,22 @@ __global__ __launch_bounds__(1024) void k_route(const int32_t* ids, int P, int E
     rv.n_slots()[0] = ns;
   }
   __syncthreads();
-  for (int p = t; p < P; p += blockDim.x) {
-    int e = ids[p];
-    if (e < 0 || e >= E) e = E;
-    int pos = atomicAdd(&cur[e], 1);
-    rv.perm()[pos] = p;
+  for (int p0 = t; p0 < P; p0 += RB * (int)blockDim.x) {
+    int ev[RB];
+#pragma unroll
+    for (int j = 0; j < RB; j++) {
+      const int p = p0 + j * (int)blockDim.x;
+      ev[j] = p < P ? ids[p] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < RB; j++) {
+      const int p = p0 + j * (int)blockDim.x;
+      if (p >= P) break;
+      int e = ev[j];
+      if (e < 0 || e >= E) e = E;
+      const int pos = atomicAdd(&cur[e], 1);
+      rv.perm()[pos] = p;
+    }
   }
 }
 
