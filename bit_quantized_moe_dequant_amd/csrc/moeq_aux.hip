@@ -227,17 +227,44 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const void* x, int T, int K
     int Ei = e + 127;
     E = (uint32_t)(Ei < 0 ? 0 : (Ei > 254 ? 254 : Ei));
   }
-  const int shift = 127 - (int)E;
+  // The hardware conversion with the block scale as its scale operand (the e8m0
+  // code in a float's exponent field) divides by 2^(E - 127) and rounds to nearest
+  // even onto E4M3FN, as e4m3_rne does for every finite value: under this exponent
+  // rule a finite value never exceeds 448 after scaling. Infinities and NaNs, which
+  // the conversion turns into NaN codes, saturate to 448 with their sign as in
+  // e4m3_rne. Blocks whose maximum is below 2^-105 take e4m3_rne itself: only there
+  // can an fp32 subnormal element scale into E4M3's range, and the conversion's
+  // handling of subnormal inputs is not relied on.
   uint32_t out[8];
+  if (ab < 0x0B000000u) {
+    const int shift = 127 - (int)E;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    uint32_t w = 0;
+    for (int i = 0; i < 8; i++) {
+      uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t c = (amax == 0.f) ? 0u : e4m3_rne(__builtin_ldexpf(v[4 * i + j], shift));
-      w |= c << (8 * j);
+      for (int j = 0; j < 4; j++) {
+        const uint32_t c = (amax == 0.f) ? 0u : e4m3_rne(__builtin_ldexpf(v[4 * i + j], shift));
+        w |= c << (8 * j);
+      }
+      out[i] = w;
     }
-    out[i] = w;
+  } else {
+    const float scale = u2f(E << 23);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      typedef short i16x2_t __attribute__((ext_vector_type(2)));
+      const i16x2_t lo =
+          __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, v[4 * i], v[4 * i + 1], scale, false);
+      const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v[4 * i + 2], v[4 * i + 3], scale, true);
+      uint32_t w = __builtin_bit_cast(uint32_t, hi);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float a = v[4 * i + j];
+        if (!(__builtin_fabsf(a) <= 3.402823466e38f))
+          w = (w & ~(0xFFu << (8 * j))) | ((0x7Eu | ((f2u(a) >> 24) & 0x80u)) << (8 * j));
+      }
+      out[i] = w;
+    }
   }
   u32x4* qo = reinterpret_cast<u32x4*>(q + b * 32);
   qo[0] = u32x4{out[0], out[1], out[2], out[3]};

@@ -162,6 +162,14 @@ def test_quantize_mxfp8_bit_exact(kind):
     v[3, :32] = np.float32(2.0 ** -130)   # subnormal block maximum
     v[4, 5] = -1e-30                      # tiny negative in a normal block
     v[5, :32] = 2.0 ** 120                # large scale
+    # block maximum 448 (scale 1): exact halfway points between E4M3 neighbours, which
+    # round to the even code (1.0625 -> 1, 1.1875 -> 1.25, 17 -> 16, 19 -> 20, and
+    # the subnormal 3 2^-10 -> 2^-8), with their negatives
+    ties = np.array([1.0625, 1.1875, 17.0, 19.0, 3.0 * 2.0 ** -10, 0.5 + 2.0 ** -5], np.float32)
+    v[6, :32] = 0.0
+    v[6, 0] = 448.0
+    v[6, 1:1 + ties.size] = ties
+    v[6, 1 + ties.size:1 + 2 * ties.size] = -ties
     if kind == "bf16":
         bits = synth.bf16_bits_from_f32(v)
         x = x_tensor(bits)
