@@ -205,6 +205,7 @@ SMALL = [
     (2, 1, 512, 128, 3, 2),     # ... and a single wave of K steps
     (2, 3, 4096, 256, 4, 2),    # K = 4096 in NVFP4: two chunks per lane; at T = 16 the 2-token gate/up tiles
     (1, 1, 4096, 256, 4, 2),    # ... and in MXFP4
+    (1, 1, 8192, 128, 4, 2),    # K = 8192: four chunks per lane (one-token gate/up tiles at any T)
 ]
 
 
