@@ -423,3 +423,108 @@ def test_rel_err_floor():
     assert moe.rel_err(ref, ref) == 0.0
     assert abs(moe.rel_err(ref + np.array([0, 0, 1e-3]), ref) - 1e-3 / 1.0) < 1e-12 or \
         moe.rel_err(ref + np.array([0, 0, 1e-3]), ref) <= 1e-3 / np.sqrt(np.mean(ref ** 2)) + 1e-12
+
+
+# ---------------------------------------------------------------- W4A8 prefill stages
+# The prefill chain (1x Spark forum thread, second post: fp4 weights times E4M3
+# activations) is checked stage by stage against moe.prefill_h / moe.prefill_y, so
+# those two functions are pinned here against the layer (when quantisation is
+# lossless) and against exact rational arithmetic.
+
+def _mxfp8_exact_rows(rng, rows, K, e_lo=118, e_hi=132):
+    """Random rows whose every 32-block is exactly E4M3 x 2^(E-127), with the block
+    maximum in (224, 448] x 2^(E-127), so MXFP8 quantisation gives back exactly
+    these codes and scales. Returns (codes, E, exact Fractions)."""
+    codes = rng.integers(0, 0x7F, (rows, K)).astype(np.uint8)         # finite, both signs below
+    codes[codes == 0x7F] = 0x7E
+    codes |= (rng.integers(0, 2, (rows, K)) << 7).astype(np.uint8)
+    codes[codes == 0x80] = 0                                          # -0 has no rational sign
+    big = np.array([0x77, 0x78, 0x7A, 0x7C, 0x7E], np.uint8)          # 240, 256, 320, 384, 448
+    for r in range(rows):
+        for b in range(K // 32):
+            blk = codes[r, 32 * b:32 * b + 32]
+            mags = np.array([abs(enc.e4m3_frac(int(c))) for c in blk])
+            if mags.max() <= 224:
+                j = rng.integers(0, 32)
+                blk[j] = big[rng.integers(0, big.size)] | (blk[j] & 0x80)
+    E = rng.integers(e_lo, e_hi, (rows, K // 32)).astype(np.uint8)
+    exact = [[enc.e4m3_frac(int(codes[r, c])) * enc.pow2_frac(int(E[r, c // 32]) - 127) for c in range(K)]
+             for r in range(rows)]
+    return codes, E, exact
+
+
+def _frac_bf16_bits(v: Fraction) -> int:
+    b = int(np.array([float(v)], np.float32).view(np.uint32)[0])
+    assert b & 0xFFFF == 0 and Fraction(float(v)) == v
+    return b >> 16
+
+
+def test_prefill_h_equals_layer_h_on_exact_mxfp8_input():
+    mats = _tiny_layer(5, E=6)
+    weight = moe.CachedWeights(lambda p, e: formats.dequant_mxfp4(mats[(p, e)][0], mats[(p, e)][1],
+                                                                  mats[(p, e)][3], mats[(p, e)][4]))
+    rng = np.random.default_rng(21)
+    T, K = 3, 2
+    codes, E, exact = _mxfp8_exact_rows(rng, T, 64, 110, 118)
+    x_bits = np.array([[_frac_bf16_bits(v) for v in row] for row in exact], np.uint16)
+    xq, xs = mxfp8.quantize(codecs.bf16_to_f64(x_bits))
+    assert np.array_equal(xq, codes) and np.array_equal(xs, E)        # lossless by construction
+    ids = np.array([[0, 5], [3, 1], [4, 2]], np.int32)
+    rw = np.array([[0.7, 0.3], [0.25, 0.75], [0.6, 0.4]], np.float32)
+    _, h_ref = moe.moe_layer(x_bits, ids, rw, weight)
+    h = moe.prefill_h(xq, xs, ids, weight)
+    assert np.array_equal(h, h_ref)
+
+
+def test_prefill_y_equals_layer_combine_on_exact_mxfp8_h():
+    # With h exactly MXFP8, prefill_y is the layer's route-weighted down combine.
+    mats = _tiny_layer(6, E=5)
+    weight = moe.CachedWeights(lambda p, e: formats.dequant_mxfp4(mats[(p, e)][0], mats[(p, e)][1],
+                                                                  mats[(p, e)][3], mats[(p, e)][4]))
+    rng = np.random.default_rng(22)
+    T, K = 3, 2
+    hq, hs, _ = _mxfp8_exact_rows(rng, T * K, 32)
+    Hh = mxfp8.dequantize(hq, hs)
+    rq, rs = mxfp8.quantize(Hh)
+    assert np.array_equal(rq, hq) and np.array_equal(rs, hs)
+    ids = np.array([[1, 4], [0, 2], [3, 0]], np.int32)
+    rw = np.array([[0.9, 0.1], [0.2, 0.8], [0.35, 0.65]], np.float32)
+    y = moe.prefill_y(hq, hs, ids, rw, weight)
+    ref = np.zeros((T, 64))
+    for t in range(T):
+        for k in range(K):
+            ref[t] += float(rw[t, k]) * (weight(moe.DOWN, ids[t, k]) @ Hh[t * K + k])
+    assert np.array_equal(y, ref)
+
+
+def test_prefill_stages_match_exact_rationals():
+    # T = 2 tokens, K = 2 distinct experts per token, asymmetric route weights: a
+    # swapped gate/up, a k*T + t row order for h or a dropped route weight all move
+    # the result far beyond the tolerance below.
+    H, I = 64, 32
+    mats = _tiny_layer(7, H=H, I=I, E=4)
+    weight = moe.CachedWeights(lambda p, e: formats.dequant_mxfp4(mats[(p, e)][0], mats[(p, e)][1],
+                                                                  mats[(p, e)][3], mats[(p, e)][4]))
+    rng = np.random.default_rng(23)
+    T, K = 2, 2
+    xq, xs, xe = _mxfp8_exact_rows(rng, T, H, 110, 118)
+    ids = np.array([[2, 0], [1, 3]], np.int32)
+    rw = np.array([[0.8125, 0.1875], [0.375, 0.625]], np.float32)
+    h = moe.prefill_h(xq, xs, ids, weight)
+    for t in range(T):
+        for k in range(K):
+            G, U = mats[(0, int(ids[t, k]))][2], mats[(1, int(ids[t, k]))][2]
+            for i in range(I):
+                g = sum(G[i][j] * xe[t][j] for j in range(H))
+                u = sum(U[i][j] * xe[t][j] for j in range(H))
+                want = float(g) / (1.0 + math.exp(-float(g))) * float(u)
+                assert abs(h[t, k, i] - want) <= 1e-13 * max(1.0, abs(want))
+    hq, hs, he = _mxfp8_exact_rows(rng, T * K, I, 118, 126)
+    y = moe.prefill_y(hq, hs, ids, rw, weight)
+    for t in range(T):
+        for r in range(H):
+            want = Fraction(0)
+            for k in range(K):
+                D = mats[(2, int(ids[t, k]))][2]
+                want += Fraction(float(rw[t, k])) * sum(D[r][j] * he[t * K + k][j] for j in range(I))
+            assert abs(y[t, r] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
