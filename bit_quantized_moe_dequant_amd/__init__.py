@@ -26,6 +26,7 @@ FMT_MXFP4, FMT_NVFP4, FMT_Q2_K, FMT_IQ2_XXS, FMT_FP8_B128 = 1, 2, 3, 4, 5
 FMT_BY_NAME = {"mxfp4": 1, "nvfp4": 2, "q2_k": 3, "iq2_xxs": 4, "fp8_b128": 5}
 
 MOEQ_OK = 0
+ABI_VERSION = 2
 DEVERR_EXPERT_ID = 1
 
 
@@ -68,7 +69,7 @@ _SIGS = {
     "moeq_prefill_gate_up": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moeq_prefill_down": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "moeq_linear": (_i, [ctypes.POINTER(MoeqWeight), _i, _vp, _i, _vp, _vp]),
-    "moeq_quantize_mxfp8_bf16": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "moeq_quantize_mxfp8": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moeq_quantize_mxfp8_f32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moeq_check_device_error": (_i, [_vp, _vp, ctypes.POINTER(ctypes.c_uint32), _i]),
     "moeq_synth_fill": (_i, [_vp, _sz, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, _i, _vp, _vp]),
@@ -91,7 +92,7 @@ def _lib():
             f = getattr(lib, name)
             f.restype = res
             f.argtypes = args
-        if lib.moeq_abi_version() != 1:
+        if lib.moeq_abi_version() != ABI_VERSION:
             raise RuntimeError("libmoeq.so ABI version mismatch")
         _LIB = lib
     return _LIB
@@ -129,6 +130,45 @@ def _require_cuda(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
             raise ValueError("tensor must be on the GPU")
+
+
+def _want(name, t, dtypes, shape):
+    """Raise ValueError unless t is a contiguous tensor of one of `dtypes` with
+    exactly `shape` (whether it is on the GPU is checked after all of them). The C ABI sees raw pointers only, so a wrong dtype (int64 ids
+    read as pairs of int32), a short buffer or a strided view must be caught here,
+    before anything is launched."""
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _tokens(name, t, width):
+    """Number of rows of a [T, width] tensor (before its full check)."""
+    if t is None or not hasattr(t, "shape") or len(t.shape) != 2 or t.shape[1] != width:
+        raise ValueError(f"{name}: expected shape (T, {width}), got {None if t is None else tuple(t.shape)}")
+    return int(t.shape[0])
+
+
+def _want_ws(layer, T, ws):
+    torch = _torch()
+    _want("ws", ws, (torch.uint8,), (ws.numel(),) if ws is not None and ws.dim() == 1 else (-1,))
+    if ws.numel() < workspace_bytes(layer, T):
+        raise ValueError(f"ws: {ws.numel()} bytes, need {workspace_bytes(layer, T)}")
+
+
+def _routing_args(layer, T, ids, rw=None):
+    torch = _torch()
+    _want("ids", ids, (torch.int32,), (T, layer.top_k))
+    if rw is not None:
+        _want("rw", rw, (torch.float32,), (T, layer.top_k))
 
 
 def plane_bytes(fmt: int, rows: int, cols: int, plane: int) -> int:
@@ -222,42 +262,56 @@ def dequant(w: Weight, expert: int, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty((w.rows, w.cols), dtype=torch.float32, device="cuda")
+    _want("out", out, (torch.float32,), (w.rows, w.cols))
     s = w.struct()
+    _require_cuda(out)
     _check("moeq_dequant", _lib().moeq_dequant(ctypes.byref(s), expert, _ptr(out), _stream_ptr()))
     return out
 
 
 def expert_forward(layer: Layer, x, ids, rw, y=None, ws=None):
     torch = _torch()
-    T = x.shape[0]
-    _require_cuda(x, ids, rw)
+    T = _tokens("x", x, layer.hidden)
+    _want("x", x, (torch.bfloat16,), (T, layer.hidden))
+    _routing_args(layer, T, ids, rw)
     if y is None:
         y = torch.empty((T, layer.hidden), dtype=torch.float32, device="cuda")
+    _want("y", y, (torch.float32,), (T, layer.hidden))
     if ws is None:
         ws = layer.workspace(T)
+    _want_ws(layer, T, ws)
     L = layer.struct()
+    _require_cuda(x, ids, rw, y, ws)
     _check("moeq_expert_forward", _lib().moeq_expert_forward(ctypes.byref(L), _ptr(x), _ptr(ids), _ptr(rw), T,
                                                               _ptr(y), _ptr(ws), ws.numel(), _stream_ptr()))
     return y
 
 
 def route(layer: Layer, ids, ws=None):
-    T = ids.shape[0]
+    T = _tokens("ids", ids, layer.top_k)
+    _routing_args(layer, T, ids)
     if ws is None:
         ws = layer.workspace(T)
+    _want_ws(layer, T, ws)
     L = layer.struct()
+    _require_cuda(ids, ws)
     _check("moeq_route", _lib().moeq_route(ctypes.byref(L), _ptr(ids), T, _ptr(ws), ws.numel(), _stream_ptr()))
     return ws
 
 
 def gate_up(layer: Layer, x, ids, h=None, ws=None):
     torch = _torch()
-    T = x.shape[0]
+    T = _tokens("x", x, layer.hidden)
+    _want("x", x, (torch.bfloat16,), (T, layer.hidden))
+    _routing_args(layer, T, ids)
     if h is None:
         h = torch.empty((T, layer.top_k, layer.inter), dtype=torch.float32, device="cuda")
+    _want("h", h, (torch.float32,), (T, layer.top_k, layer.inter))
     if ws is None:
         ws = layer.workspace(T)
+    _want_ws(layer, T, ws)
     L = layer.struct()
+    _require_cuda(x, ids, h, ws)
     _check("moeq_gate_up", _lib().moeq_gate_up(ctypes.byref(L), _ptr(x), _ptr(ids), T, _ptr(h), _ptr(ws), ws.numel(),
                                                 _stream_ptr()))
     return h
@@ -267,12 +321,17 @@ def gate_up_timed(layer: Layer, x, ids, start, stop, h=None, ws=None):
     """gate_up with torch.cuda.Event objects (enable_timing=True, already recorded
     once) bracketing the kernel's own execution."""
     torch = _torch()
-    T = x.shape[0]
+    T = _tokens("x", x, layer.hidden)
+    _want("x", x, (torch.bfloat16,), (T, layer.hidden))
+    _routing_args(layer, T, ids)
     if h is None:
         h = torch.empty((T, layer.top_k, layer.inter), dtype=torch.float32, device="cuda")
+    _want("h", h, (torch.float32,), (T, layer.top_k, layer.inter))
     if ws is None:
         ws = layer.workspace(T)
+    _want_ws(layer, T, ws)
     L = layer.struct()
+    _require_cuda(x, ids, h, ws)
     _check("moeq_gate_up_timed", _lib().moeq_gate_up_timed(ctypes.byref(L), _ptr(x), _ptr(ids), T, _ptr(h), _ptr(ws),
                                                             ws.numel(), _stream_ptr(),
                                                             ctypes.c_void_p(start.cuda_event),
@@ -282,12 +341,17 @@ def gate_up_timed(layer: Layer, x, ids, start, stop, h=None, ws=None):
 
 def down(layer: Layer, h, ids, rw, y=None, ws=None):
     torch = _torch()
-    T = ids.shape[0]
+    T = _tokens("ids", ids, layer.top_k)
+    _routing_args(layer, T, ids, rw)
+    _want("h", h, (torch.float32,), (T, layer.top_k, layer.inter))
     if y is None:
         y = torch.empty((T, layer.hidden), dtype=torch.float32, device="cuda")
+    _want("y", y, (torch.float32,), (T, layer.hidden))
     if ws is None:
         ws = layer.workspace(T)
+    _want_ws(layer, T, ws)
     L = layer.struct()
+    _require_cuda(h, ids, rw, y, ws)
     _check("moeq_down", _lib().moeq_down(ctypes.byref(L), _ptr(h), _ptr(ids), _ptr(rw), T, _ptr(y), _ptr(ws),
                                           ws.numel(), _stream_ptr()))
     return y
@@ -295,15 +359,24 @@ def down(layer: Layer, h, ids, rw, y=None, ws=None):
 
 def prefill_gate_up(layer: Layer, xq, xs, ids, hq=None, hs=None, h_f32=None, ws=None):
     torch = _torch()
-    T = xq.shape[0]
+    T = _tokens("xq", xq, layer.hidden)
     P = T * layer.top_k
+    _want("xq", xq, (torch.uint8,), (T, layer.hidden))
+    _want("xs", xs, (torch.uint8,), (T, layer.hidden // 32))
+    _routing_args(layer, T, ids)
     if hq is None:
         hq = torch.empty((P, layer.inter), dtype=torch.uint8, device="cuda")
     if hs is None:
         hs = torch.empty((P, layer.inter // 32), dtype=torch.uint8, device="cuda")
+    _want("hq", hq, (torch.uint8,), (P, layer.inter))
+    _want("hs", hs, (torch.uint8,), (P, layer.inter // 32))
+    if h_f32 is not None:
+        _want("h_f32", h_f32, (torch.float32,), (P, layer.inter))
     if ws is None:
         ws = layer.workspace(T)
+    _want_ws(layer, T, ws)
     L = layer.struct()
+    _require_cuda(xq, xs, ids, hq, hs, h_f32, ws)
     _check("moeq_prefill_gate_up", _lib().moeq_prefill_gate_up(ctypes.byref(L), _ptr(xq), _ptr(xs), _ptr(ids), T,
                                                                 _ptr(h_f32), _ptr(hq), _ptr(hs), _ptr(ws), ws.numel(),
                                                                 _stream_ptr()))
@@ -312,12 +385,19 @@ def prefill_gate_up(layer: Layer, xq, xs, ids, hq=None, hs=None, h_f32=None, ws=
 
 def prefill_down(layer: Layer, hq, hs, ids, rw, y=None, ws=None):
     torch = _torch()
-    T = ids.shape[0]
+    T = _tokens("ids", ids, layer.top_k)
+    P = T * layer.top_k
+    _routing_args(layer, T, ids, rw)
+    _want("hq", hq, (torch.uint8,), (P, layer.inter))
+    _want("hs", hs, (torch.uint8,), (P, layer.inter // 32))
     if y is None:
         y = torch.empty((T, layer.hidden), dtype=torch.float32, device="cuda")
+    _want("y", y, (torch.float32,), (T, layer.hidden))
     if ws is None:
         ws = layer.workspace(T)
+    _want_ws(layer, T, ws)
     L = layer.struct()
+    _require_cuda(hq, hs, ids, rw, y, ws)
     _check("moeq_prefill_down", _lib().moeq_prefill_down(ctypes.byref(L), _ptr(hq), _ptr(hs), _ptr(ids), _ptr(rw), T,
                                                           _ptr(y), _ptr(ws), ws.numel(), _stream_ptr()))
     return y
@@ -325,10 +405,13 @@ def prefill_down(layer: Layer, hq, hs, ids, rw, y=None, ws=None):
 
 def linear(w: Weight, expert: int, x, y=None):
     torch = _torch()
-    T = x.shape[0]
+    T = _tokens("x", x, w.cols)
+    _want("x", x, (torch.bfloat16,), (T, w.cols))
     if y is None:
         y = torch.empty((T, w.rows), dtype=torch.float32, device="cuda")
+    _want("y", y, (torch.float32,), (T, w.rows))
     s = w.struct()
+    _require_cuda(x, y)
     _check("moeq_linear", _lib().moeq_linear(ctypes.byref(s), expert, _ptr(x), T, _ptr(y), _stream_ptr()))
     return y
 
@@ -336,15 +419,21 @@ def linear(w: Weight, expert: int, x, y=None):
 def quantize_mxfp8(x, q=None, e=None):
     """MXFP8 codes [T, K] and e8m0 scales [T, K/32] of a bf16 or fp32 [T, K] tensor."""
     torch = _torch()
+    if x is None or len(x.shape) != 2:
+        raise ValueError("x: expected a [T, K] tensor")
     T, K = x.shape
+    _want("x", x, (torch.bfloat16, torch.float32), (T, K))
     if q is None:
         q = torch.empty((T, K), dtype=torch.uint8, device="cuda")
     if e is None:
         e = torch.empty((T, K // 32), dtype=torch.uint8, device="cuda")
+    _want("q", q, (torch.uint8,), (T, K))
+    _want("e", e, (torch.uint8,), (T, K // 32))
+    _require_cuda(x, q, e)
     if x.dtype == torch.float32:
         rc = _lib().moeq_quantize_mxfp8_f32(_ptr(x), T, K, _ptr(q), _ptr(e), _stream_ptr())
     else:
-        rc = _lib().moeq_quantize_mxfp8_bf16(_ptr(x), T, K, _ptr(q), _ptr(e), _stream_ptr())
+        rc = _lib().moeq_quantize_mxfp8(_ptr(x), T, K, _ptr(q), _ptr(e), _stream_ptr())
     _check("moeq_quantize_mxfp8", rc)
     return q, e
 

@@ -554,7 +554,7 @@ int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y
   return hip_rc(launch_gemv(w->fmt, EPI_PLAIN, p, 1, T > 1 ? 4 : 1, S(stream)));
 }
 
-int moeq_quantize_mxfp8_bf16(const void* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream) {
+int moeq_quantize_mxfp8(const void* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream) {
   if (!x || !q || !e8m0 || T < 0) return MOEQ_E_INVAL;
   if (K <= 0 || K % 32) return MOEQ_E_SHAPE;
   if (!aligned(x, 16) || !aligned(q, 16)) return MOEQ_E_ALIGN;

@@ -333,11 +333,17 @@ template <> struct Dec<FMT_Q2_K> {
       } else {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          float x0 = u2f(v[i][0]), x1 = u2f(v[i][1]);
-          float x2 = u2f(v[i][2]), x3 = u2f(v[i][3]);
-          split_pair(x0, x2, x[8 * p + 2 * i], x[32 + 8 * p + 2 * i]);
-          split_pair(x1, x3, x[8 * p + 2 * i + 1], x[32 + 8 * p + 2 * i + 1]);
-          s += (x0 + x1) + (x2 + x3);
+          uint32_t h02, l02, h13, l13;
+          split_pair(u2f(v[i][0]), u2f(v[i][2]), h02, l02);
+          split_pair(u2f(v[i][1]), u2f(v[i][3]), h13, l13);
+          x[8 * p + 2 * i] = h02;
+          x[32 + 8 * p + 2 * i] = l02;
+          x[8 * p + 2 * i + 1] = h13;
+          x[32 + 8 * p + 2 * i + 1] = l13;
+          // The bias term removed below must be the sum of exactly the values the
+          // dot products see (hi + lo), or the split's residual would not cancel.
+          s += (u2f(h02 << 16) + u2f(l02 << 16)) + (u2f(h13 << 16) + u2f(l13 << 16)) +
+               (u2f(h02 & 0xFFFF0000u) + u2f(l02 & 0xFFFF0000u)) + (u2f(h13 & 0xFFFF0000u) + u2f(l13 & 0xFFFF0000u));
         }
       }
       xs[p] = s;

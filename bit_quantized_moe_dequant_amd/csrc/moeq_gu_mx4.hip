@@ -2,8 +2,9 @@
 // block-scaled matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4, with no weight
 // decode on the VALU, and the single-token MXFP4 down projection.
 //
-// The MXFP4 weights (e2m1 codes, one e8m0 scale per 32 along K: DeepSeek-V4-Flash
-// W4A16-FP8 model card, "Architecture & precision") are the instruction's FP4
+// The MXFP4 weights (e2m1 codes, one e8m0 scale per 32 along K: DeepSeek V4 Flash -
+// REAP K180 Mixed NVFP4 card, section "NVFP4: lossless MXFP4->NVFP4 conversion";
+// DeepSeekv4 Flash for 1x Spark forum thread, first post) are the instruction's FP4
 // operand B as they sit in memory: lane (row n, group g) passes the 16-byte chunk
 // of its row at K = 32g + [0, 32) and that chunk's e8m0 as its B scale. The bf16
 // token is operand A, split into two E4M3 terms, x = hi + lo, each with an e8m0
@@ -75,7 +76,8 @@ struct MxStage {
 };
 
 // NVFP4 (e2m1 codes, an E4M3 scale per 16 along K and an fp32 scale_2 per expert
-// tensor: DeepSeek-V4-Flash NVFP4 checkpoint card, "Format") in the same
+// tensor: DeepSeek V4 Flash - REAP K180 Mixed NVFP4 card, section "NVFP4: lossless
+// MXFP4->NVFP4 conversion") in the same
 // instruction. Its block scale is not a power of two and its blocks are 16 wide,
 // so it cannot be the instruction's B scale (B scale code 127, i.e. 1). Instead
 // each row of A holds one term of x on one 16-block of the 128-wide step and zeros

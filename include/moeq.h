@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOEQ_ABI_VERSION 1
+#define MOEQ_ABI_VERSION 2
 
 /* ------------------------------------------------------------------ formats
  * Device layout of one expert tensor [rows, cols] (the `data` and `scales`
@@ -224,8 +224,13 @@ int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y
  * values, e8m0 code E = clamp(e + 127, 0, 254) with 2^e the smallest power of two
  * keeping max|v| / 2^e <= 448 (e = p-9 if the frexp mantissa of max|v| is <= 0.875,
  * else p-8; all-zero block: E = 0, codes 0); codes = E4M3FN round-to-nearest-even of
- * v / 2^(E-127), saturating, sign kept. _bf16 takes bf16 input, _f32 fp32. */
-int moeq_quantize_mxfp8_bf16(const void* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream);
+ * v / 2^(E-127), saturating, sign kept (1x Spark forum thread, second post: E4M3
+ * activations with a dynamic scale; the 32-wide block and the non-clipping scale
+ * rule are this library's reading). moeq_quantize_mxfp8 takes bf16 input x [T][K]
+ * (the prefill activations), moeq_quantize_mxfp8_f32 fp32 (the intermediate h).
+ * x and q 16-byte aligned, caller-owned device memory; q u8 [T][K] and e8m0 u8
+ * [T][K/32] overwritten. MOEQ_E_SHAPE if K is not a positive multiple of 32. */
+int moeq_quantize_mxfp8(const void* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream);
 int moeq_quantize_mxfp8_f32(const float* x, int T, int K, uint8_t* q, uint8_t* e8m0, void* stream);
 
 /* Synchronise `stream`, then read (and with clear != 0, zero) the device error word. */

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 20
     missing = [n for n in names if not hasattr(lib, n)]
     assert missing == []
-    assert mq._lib().moeq_abi_version() == 1
+    assert mq._lib().moeq_abi_version() == mq.ABI_VERSION == 2
 
 
 def test_status_strings():
@@ -91,7 +91,7 @@ def test_workspace_and_forward_validation():
 def test_quantize_validation():
     lib = mq._lib()
     p = ctypes.c_void_p(0x100000)
-    assert lib.moeq_quantize_mxfp8_bf16(p, 4, 48, p, p, None) == -4
+    assert lib.moeq_quantize_mxfp8(p, 4, 48, p, p, None) == -4
     assert lib.moeq_quantize_mxfp8_f32(p, 4, 64, ctypes.c_void_p(0x100004), p, None) == -3
     assert lib.moeq_quantize_mxfp8_f32(p, 0, 64, p, p, None) == 0
 
@@ -132,3 +132,48 @@ def test_mxfp4_to_nvfp4_host_refuses_lossy():
     assert ei.value.status == -7
     with pytest.raises(mq.MoeqError):
         mq.mxfp4_to_nvfp4(np.zeros(16, np.uint8), np.array([255], np.uint8), 1, 32)
+
+
+def _cpu_layer(H=256, I=64, E=4, K=2):
+    """A layer descriptor backed by host tensors: enough for the binding's argument
+    checks, which run before any pointer reaches the library."""
+    import torch
+    ws = []
+    for rows, cols in [(I, H), (I, H), (H, I)]:
+        p0, p1 = mq.plane_bytes(mq.FMT_MXFP4, rows, cols, 0), mq.plane_bytes(mq.FMT_MXFP4, rows, cols, 1)
+        ws.append(mq.Weight(mq.FMT_MXFP4, rows, cols, E, torch.zeros(p0 * E, dtype=torch.uint8),
+                            torch.zeros(p1 * E, dtype=torch.uint8)))
+    return mq.Layer(H, I, E, K, *ws)
+
+
+def test_binding_rejects_wrong_dtypes_and_shapes():
+    import torch
+    layer = _cpu_layer()
+    T = 3
+    x = torch.zeros((T, 256), dtype=torch.bfloat16)
+    ids = torch.zeros((T, 2), dtype=torch.int32)
+    rw = torch.zeros((T, 2), dtype=torch.float32)
+    y = torch.zeros((T, 256), dtype=torch.float32)
+    ws = torch.zeros(mq.workspace_bytes(layer, T), dtype=torch.uint8)
+    cases = [
+        dict(ids=ids.to(torch.int64)),                    # torch.topk's dtype: would be read as int32 pairs
+        dict(rw=rw.to(torch.float64)),
+        dict(rw=rw[:2]),                                  # fewer rows than tokens
+        dict(ids=torch.zeros((T, 3), dtype=torch.int32)),  # wrong top_k
+        dict(x=x.to(torch.float32)),
+        dict(x=torch.zeros((256, T), dtype=torch.bfloat16).t()),  # strided view
+        dict(y=y[:, :128]),
+        dict(ws=ws[:16]),
+    ]
+    for c in cases:
+        a = dict(x=x, ids=ids, rw=rw, y=y, ws=ws)
+        a.update(c)
+        with pytest.raises(ValueError):
+            mq.expert_forward(layer, a["x"], a["ids"], a["rw"], y=a["y"], ws=a["ws"])
+    # well-formed arguments pass every check and then stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        mq.expert_forward(layer, x, ids, rw, y=y, ws=ws)
+    with pytest.raises(ValueError):
+        mq.down(layer, torch.zeros((T, 2, 32), dtype=torch.float32), ids, rw, y=y, ws=ws)
+    with pytest.raises(ValueError):
+        mq.gate_up(layer, x, ids.to(torch.int64), ws=ws)
