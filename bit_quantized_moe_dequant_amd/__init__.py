@@ -26,6 +26,8 @@ FMT_MXFP4, FMT_NVFP4, FMT_Q2_K, FMT_IQ2_XXS, FMT_FP8_B128 = 1, 2, 3, 4, 5
 FMT_BY_NAME = {"mxfp4": 1, "nvfp4": 2, "q2_k": 3, "iq2_xxs": 4, "fp8_b128": 5}
 
 MOEQ_OK = 0
+MOEQ_E_SCRATCH = -8
+NOALLOC_SCRATCH_BYTES = 32 << 20
 ABI_VERSION = 2
 DEVERR_EXPERT_ID = 1
 
@@ -62,6 +64,7 @@ _SIGS = {
     "moeq_workspace_bytes": (_sz, [ctypes.POINTER(MoeqLayer), _i]),
     "moeq_workspace_init": (_i, [_vp, _sz, _vp]),
     "moeq_expert_forward": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
+    "moeq_expert_forward_noalloc": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "moeq_route": (_i, [ctypes.POINTER(MoeqLayer), _vp, _i, _vp, _sz, _vp]),
     "moeq_gate_up": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "moeq_down": (_i, [ctypes.POINTER(MoeqLayer), _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
@@ -284,6 +287,28 @@ def expert_forward(layer: Layer, x, ids, rw, y=None, ws=None):
     _require_cuda(x, ids, rw, y, ws)
     _check("moeq_expert_forward", _lib().moeq_expert_forward(ctypes.byref(L), _ptr(x), _ptr(ids), _ptr(rw), T,
                                                               _ptr(y), _ptr(ws), ws.numel(), _stream_ptr()))
+    return y
+
+
+def expert_forward_noalloc(layer: Layer, x, ids, rw, y=None, dev_err=None):
+    """moeq_expert_forward_noalloc: the forward with the library's fixed device
+    scratch instead of a workspace (nothing allocated by the library; y is
+    allocated here only when not given). dev_err: optional int32/uint32 [1] device
+    tensor that receives the device error bits by OR."""
+    torch = _torch()
+    T = _tokens("x", x, layer.hidden)
+    _want("x", x, (torch.bfloat16,), (T, layer.hidden))
+    _routing_args(layer, T, ids, rw)
+    if y is None:
+        y = torch.empty((T, layer.hidden), dtype=torch.float32, device="cuda")
+    _want("y", y, (torch.float32,), (T, layer.hidden))
+    if dev_err is not None:
+        _want("dev_err", dev_err, (torch.int32, torch.uint32), (1,))
+    L = layer.struct()
+    _require_cuda(x, ids, rw, y, dev_err)
+    _check("moeq_expert_forward_noalloc",
+           _lib().moeq_expert_forward_noalloc(ctypes.byref(L), _ptr(x), _ptr(ids), _ptr(rw), T, _ptr(y),
+                                              _ptr(dev_err), _stream_ptr()))
     return y
 
 

@@ -8,6 +8,7 @@
 #include "moeq_kernels.h"
 
 #include <cmath>
+#include <mutex>
 
 using namespace moeq;
 
@@ -104,6 +105,7 @@ bool prefill_path(const moeq_layer* L, int T) {
 struct WsLayout {
   size_t route, h, partial, xq, xs, hq, hs, total;
   int P;
+  uint32_t* err;  // device error word the kernels OR into (null: the workspace's own)
 };
 
 WsLayout ws_layout(const moeq_layer* L, int T) {
@@ -118,6 +120,7 @@ WsLayout ws_layout(const moeq_layer* L, int T) {
   w.partial = off;
   off += T > 1 ? align_up(P * L->hidden * 4, 256) : 0;
   w.xq = w.xs = w.hq = w.hs = 0;
+  w.err = nullptr;
   if (prefill_path(L, T)) {
     w.xq = off;
     off += align_up((size_t)T * L->hidden, 256);
@@ -142,6 +145,7 @@ int check_ws(const moeq_layer* L, int T, void* ws, size_t ws_bytes) {
 inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOEQ_OK : MOEQ_E_HIP; }
 inline hipStream_t S(void* s) { return (hipStream_t)s; }
 inline uint32_t* err_word(void* ws) { return (uint32_t*)ws; }
+inline uint32_t* err_of(void* ws, const WsLayout& lay) { return lay.err ? lay.err : err_word(ws); }
 inline RouteView route_view(const moeq_layer* L, void* ws, const WsLayout& lay) {
   RouteView rv;
   rv.base = (int32_t*)((uint8_t*)ws + lay.route);
@@ -163,7 +167,7 @@ GemvParams gemv_params(const moeq_layer* L, const moeq_weight& a, const moeq_wei
   p.top_k = L ? L->top_k : 1;
   if (ws) {
     p.route = route_view(L, ws, lay);
-    p.err = err_word(ws);
+    p.err = err_of(ws, lay);
   }
   return p;
 }
@@ -235,7 +239,7 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
     d.ids = ids;
     d.rw = rw;
     d.y = y;
-    d.err = err_word(ws);
+    d.err = err_of(ws, lay);
     return hip_rc(launch_down1(L->down.fmt, d, s));
   }
   GemvParams p = gemv_params(L, L->down, nullptr, ws, lay);
@@ -320,6 +324,34 @@ int run_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, 
   return hip_rc(launch_combine(partial, T, L->top_k, L->hidden, y, s));
 }
 
+int forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y, void* ws,
+            const WsLayout& lay, hipStream_t s);
+
+// ---------------------------------------------------------------- allocation-free scratch
+// Device memory of moeq_expert_forward_noalloc: a file-scope array that each GPU
+// holds for the life of the process (no hipMalloc on any call). Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address is taken once per device with hipGetSymbolAddress,
+// with that device current, and kept here.
+__device__ __align__(256) uint8_t scratch[MOEQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return MOEQ_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOEQ_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOEQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,6 +368,7 @@ const char* moeq_status_string(int status) {
     case MOEQ_E_WORKSPACE: return "workspace missing or too small";
     case MOEQ_E_HIP: return "HIP launch or runtime error";
     case MOEQ_E_LOSSY: return "conversion would not be exact";
+    case MOEQ_E_SCRATCH: return "workspace needed exceeds the allocation-free scratch (MOEQ_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -477,11 +510,34 @@ int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, 
   if (!aligned(x, 16) || !aligned(y, 16)) return MOEQ_E_ALIGN;
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
   if (T == 0) return MOEQ_OK;
+  return forward(L, x, ids, rw, T, y, ws, ws_layout(L, T), S(stream));
+}
+
+int moeq_expert_forward_noalloc(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T,
+                                float* y, uint32_t* dev_err, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0 || !x || !ids || !rw || !y) return MOEQ_E_INVAL;
+  if (!aligned(x, 16) || !aligned(y, 16) || (dev_err && !aligned(dev_err, 4))) return MOEQ_E_ALIGN;
   WsLayout lay = ws_layout(L, T);
-  hipStream_t s = S(stream);
+  if (lay.total > MOEQ_NOALLOC_SCRATCH_BYTES) return MOEQ_E_SCRATCH;
+  if (T == 0) return MOEQ_OK;
+  void* ws = nullptr;
+  if ((rc = noalloc_scratch(&ws))) return rc;
+  lay.err = dev_err;  // null: the scratch's own word, which nothing reads
+  return forward(L, x, ids, rw, T, y, ws, lay, S(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y, void* ws,
+            const WsLayout& lay, hipStream_t s) {
+  int rc;
   float* h = (float*)((uint8_t*)ws + lay.h);
   if (T > 1) {
-    rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_word(ws), s));
+    rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_of(ws, lay), s));
     if (rc) return rc;
   }
   if (prefill_path(L, T) && check_prefill(L) == MOEQ_OK && prefill_a_fits(L, T)) {
@@ -496,6 +552,10 @@ int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, 
   if ((rc = run_gate_up(L, x, ids, T, h, ws, lay, s))) return rc;
   return run_down(L, h, ids, rw, T, y, ws, lay, s);
 }
+
+}  // namespace
+
+extern "C" {
 
 int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* xs, const int32_t* ids, int T,
                          float* h_f32, uint8_t* hq, uint8_t* hs, void* ws, size_t ws_bytes, void* stream) {

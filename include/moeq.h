@@ -99,6 +99,7 @@ extern "C" {
 #define MOEQ_E_WORKSPACE -5 /* workspace missing or smaller than moeq_workspace_bytes */
 #define MOEQ_E_HIP -6       /* a HIP call or kernel launch failed */
 #define MOEQ_E_LOSSY -7     /* MXFP4 -> NVFP4 cannot be exact (span > 17 or NaN scale) */
+#define MOEQ_E_SCRATCH -8   /* moeq_expert_forward_noalloc: the call needs more than the scratch holds */
 
 /* Bits of the device error word (first 4 bytes of a workspace). */
 #define MOEQ_DEVERR_EXPERT_ID 1u /* an expert id was outside [0, n_experts) */
@@ -177,6 +178,25 @@ int moeq_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * quantised to MXFP8). T == 0 is a no-op. x, y 16-byte aligned. */
 int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* moeq_expert_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It runs the same kernels on the same path,
+ * with their scratch (routing, h, partials, MXFP8 buffers) in a fixed device
+ * array inside the library: MOEQ_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ * process ends, its address taken once per device on the first call. No call
+ * allocates or frees anything. A call whose moeq_workspace_bytes(L, T) exceeds
+ * the scratch returns MOEQ_E_SCRATCH before any launch (at hidden 4096,
+ * intermediate 2048, 256 experts, top-6: up to T = 227 tokens on the decode path;
+ * an all-MXFP4 layer takes the prefill path from T = 128, up to T = 204). Every call on a GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (two streams, or two threads) race and must be
+ * serialised by the caller; nothing in the scratch has to start at zero.
+ * dev_err (device memory, 4-byte aligned, may be NULL) receives the
+ * MOEQ_DEVERR_* bits by OR; with NULL they go to a word nobody reads. Other
+ * arguments, checks and outputs as moeq_expert_forward. */
+#define MOEQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int moeq_expert_forward_noalloc(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T,
+                                float* y, uint32_t* dev_err, void* stream);
 
 /* Stages of the decode path, for tests and timing (moeq_expert_forward runs them
  * in order). moeq_route groups the T*K (token, slot) pairs by expert into the

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = mq._lib()
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert lib.moeq_status_string(code) != b"unknown status"
 
 
