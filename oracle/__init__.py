@@ -9,8 +9,9 @@ imports nothing from it; inputs come from the caller.
 
 Modules:
   codecs   element codecs (e2m1, e4m3fn, e8m0, fp16, bf16) from their definitions
-  formats  per-format decode of whole expert tensors (source layouts) and sizes
-  convert  the lossless MXFP4 -> NVFP4 re-encode
+  formats  per-format decode of whole tensors (source layouts) and sizes: MXFP4,
+           NVFP4, Q2_K, IQ2_XXS, FP8 block-128, FP8 block-32, MXFP8
+  convert  the lossless MXFP4 -> NVFP4 re-encode and its exact inverse
   mxfp8    MXFP8 activation quantisation (E4M3 elements, e8m0 per 32)
   moe      routed-MoE layer, dense FP8 linear, and the W4A8 prefill chain
 

@@ -1,4 +1,4 @@
-"""Lossless MXFP4 -> NVFP4 re-encode of an expert tensor.
+"""Lossless MXFP4 -> NVFP4 re-encode of an expert tensor, and its inverse.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -16,6 +16,12 @@ chosen so that the largest block exponent lands on e4m3's largest power of two,
 so e4m3 * scale_2 = 2^(E - 127) exactly. e4m3 holds every power of two from 2^-9
 (smallest subnormal) to 2^8, so the re-encode is exact when Emax - E <= 17 for
 every block; a wider span, or a NaN code (255), cannot be carried and is refused.
+
+The inverse (NVFP4 -> MXFP4, so that an NVFP4 tensor can take a path built for
+e8m0 block scales) is exact exactly when, in every 32-block, both 16-halves carry
+the same e4m3 scale and that scale times scale_2 is a power of two 2^k with
+-127 <= k <= 127 (then E = k + 127); otherwise it is refused. It undoes the
+forward re-encode byte for byte.
 """
 from __future__ import annotations
 
@@ -49,3 +55,28 @@ def mxfp4_to_nvfp4(nib, e8m0, rows: int, cols: int):
                         for E in range(256)], dtype=np.uint8)
     e4m3 = np.repeat(codes32[e], 2, axis=1)   # both 16-halves of each 32-block
     return nib.copy(), e4m3, scale2
+
+
+def nvfp4_to_mxfp4(nib, e4m3, scale2, rows: int, cols: int):
+    """Returns (nibbles u8 [rows, cols/2], e8m0 u8 [rows, cols/32]) or raises
+    LossyConversion when some block has no exact e8m0 scale."""
+    from fractions import Fraction
+
+    from .codecs import E4M3
+
+    nib = np.asarray(nib, dtype=np.uint8).reshape(rows, cols // 2)
+    s = np.asarray(e4m3, dtype=np.uint8).reshape(rows, cols // 32, 2)
+    if np.any(s[..., 0] != s[..., 1]):
+        raise LossyConversion("the two 16-halves of a block carry different scales")
+    s2 = Fraction(float(np.float32(scale2)))
+    e8 = np.empty((rows, cols // 32), dtype=np.uint8)
+    for code in np.unique(s[..., 0]):
+        v = E4M3[int(code)]
+        if not np.isfinite(v) or v <= 0:
+            raise LossyConversion(f"e4m3 scale code {int(code):#x} is not a positive number")
+        p = Fraction(float(v)) * s2
+        k = p.numerator.bit_length() - 1 if p.denominator == 1 else -(p.denominator.bit_length() - 1)
+        if p != Fraction(2) ** k or not -127 <= k <= 127:
+            raise LossyConversion(f"scale {p} is not a power of two in e8m0's range")
+        e8[s[..., 0] == code] = k + 127
+    return nib.copy(), e8

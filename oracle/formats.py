@@ -30,6 +30,16 @@ Formats and the passages that define them:
   * FP8 block-128 - E4M3 weights with one UE8M0 scale per 128 x 128 tile, 8 bits
     per weight (IQ2_XXS + Q2_K + FP8 hybrid card, format table; DeepSeek-V4-Flash
     W4A16-FP8 card, component precisions table: FP8 block 128 x 128).
+  * FP8 block-32 - the same with one UE8M0 scale per 32 x 32 tile: the dense FP8
+    weights of DeepSeek-V4.1 (DeepSeek-V4.1-Flash mixed-Q2 GGUF card, Recipe,
+    second bullet: V4.1 uses 32 x 32 E8M0 block scales where V4 uses 128 x 128,
+    and reading one with the other's tile size rescales every weight).
+    8 + 8/1024 bits per weight.
+  * MXFP8 - E4M3 elements with one e8m0 scale per 32 along the input axis, the
+    checkpoint's own format for attention, shared experts and the head
+    (DeepSeekv4 Flash for 1x Spark forum thread, first post; second post: the
+    same bytes pre-stored in the matrix engine's layout). 8.25 bits per weight.
+    Source layout: codes u8 [rows, cols], e8m0 u8 [rows, cols/32].
 
 Readings where the pages are silent (each listed in the design notes):
   * Q2_K block = scales[16] u8, qs[64] u8, d fp16, dmin fp16 (little-endian).
@@ -43,7 +53,10 @@ Readings where the pages are silent (each listed in the design notes):
     is the 7-bit code with bit 7 set to the parity of the code (so every group has
     an even number of negative weights); bit j set negates weight j.
   * FP8 tiles are 2-D 128 x 128 (8.0005 bits per weight; a 1 x 128 tiling would
-    give 8.0625).
+    give 8.0625); the V4.1 tiles likewise 2-D 32 x 32.
+  * MXFP8 elements and scales follow the OCP MX definition (E4M3FN elements, a
+    shared power-of-two scale 2^(E-127), E = 255 NaN) with the block along the
+    input axis, as for MXFP4 in the same checkpoint.
 """
 from __future__ import annotations
 
@@ -51,8 +64,8 @@ import numpy as np
 
 from .codecs import E2M1, E4M3, E8M0, fp16_to_f64
 
-MXFP4, NVFP4, Q2_K, IQ2_XXS, FP8_B128 = 1, 2, 3, 4, 5
-BLOCK_K = {MXFP4: 32, NVFP4: 16, Q2_K: 256, IQ2_XXS: 256, FP8_B128: 128}
+MXFP4, NVFP4, Q2_K, IQ2_XXS, FP8_B128, MXFP8, FP8_B32 = 1, 2, 3, 4, 5, 6, 7
+BLOCK_K = {MXFP4: 32, NVFP4: 16, Q2_K: 256, IQ2_XXS: 256, FP8_B128: 128, MXFP8: 32, FP8_B32: 32}
 
 
 def packed_bytes(fmt: int, rows: int, cols: int) -> int:
@@ -74,6 +87,12 @@ def packed_bytes(fmt: int, rows: int, cols: int) -> int:
         if rows % 128:
             return 0
         return n + (rows // 128) * (cols // 128)
+    if fmt == FP8_B32:
+        if rows % 32:
+            return 0
+        return n + (rows // 32) * (cols // 32)
+    if fmt == MXFP8:
+        return n + n // 32
     return 0
 
 
@@ -151,6 +170,18 @@ def dequant_fp8_b128(q, s, rows: int, cols: int) -> np.ndarray:
     return v * np.repeat(np.repeat(sc, 128, axis=0), 128, axis=1)
 
 
+def dequant_fp8_b32(q, s, rows: int, cols: int) -> np.ndarray:
+    v = E4M3[np.asarray(q, dtype=np.uint8).reshape(rows, cols)]
+    sc = E8M0[np.asarray(s, dtype=np.uint8).reshape(rows // 32, cols // 32)]
+    return v * np.repeat(np.repeat(sc, 32, axis=0), 32, axis=1)
+
+
+def dequant_mxfp8(q, e8m0, rows: int, cols: int) -> np.ndarray:
+    v = E4M3[np.asarray(q, dtype=np.uint8).reshape(rows, cols)]
+    s = E8M0[np.asarray(e8m0, dtype=np.uint8).reshape(rows, cols // 32)]
+    return v * np.repeat(s, 32, axis=1)
+
+
 def dequant(fmt: int, planes, rows: int, cols: int, scale2: float = 1.0, grid=None) -> np.ndarray:
     """Dispatch on format; ``planes`` is the list of source-layout arrays."""
     if fmt == MXFP4:
@@ -163,6 +194,10 @@ def dequant(fmt: int, planes, rows: int, cols: int, scale2: float = 1.0, grid=No
         return dequant_iq2_xxs(planes[0], grid, rows, cols)
     if fmt == FP8_B128:
         return dequant_fp8_b128(planes[0], planes[1], rows, cols)
+    if fmt == FP8_B32:
+        return dequant_fp8_b32(planes[0], planes[1], rows, cols)
+    if fmt == MXFP8:
+        return dequant_mxfp8(planes[0], planes[1], rows, cols)
     raise ValueError(fmt)
 
 

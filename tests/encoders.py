@@ -118,3 +118,19 @@ def encode_fp8_b128(codes, S, rows, cols):
     exact = [[e4m3_frac(int(q[r, c])) * pow2_frac(int(S[r // 128][c // 128]) - 127) for c in range(cols)]
              for r in range(rows)]
     return q.reshape(-1), np.array(S, np.uint8).reshape(-1), exact
+
+
+def encode_mxfp8(codes, E, rows, cols):
+    """codes [rows][cols] E4M3 codes, E [rows][cols/32] e8m0 codes."""
+    q = np.array(codes, np.uint8).reshape(rows, cols)
+    exact = [[e4m3_frac(int(q[r, c])) * pow2_frac(int(E[r][c // 32]) - 127) for c in range(cols)]
+             for r in range(rows)]
+    return q.reshape(-1), np.array(E, np.uint8).reshape(-1), exact
+
+
+def encode_fp8_b32(codes, S, rows, cols):
+    """codes [rows][cols] E4M3 codes, S [rows/32][cols/32] e8m0 codes of the tiles."""
+    q = np.array(codes, np.uint8).reshape(rows, cols)
+    exact = [[e4m3_frac(int(q[r, c])) * pow2_frac(int(S[r // 32][c // 32]) - 127) for c in range(cols)]
+             for r in range(rows)]
+    return q.reshape(-1), np.array(S, np.uint8).reshape(-1), exact

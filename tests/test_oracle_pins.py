@@ -528,3 +528,116 @@ def test_prefill_stages_match_exact_rationals():
                 D = mats[(2, int(ids[t, k]))][2]
                 want += Fraction(float(rw[t, k])) * sum(D[r][j] * he[t * K + k][j] for j in range(I))
             assert abs(y[t, r] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
+
+
+# ---------------------------------------------------------------- MXFP8 and V4.1 FP8 tiles
+
+def test_worked_fp8_b32():
+    g = load("worked_blocks.json")["fp8_b32"]
+    q = np.zeros((g["rows"], g["cols"]), np.uint8)
+    for k, v in g["codes_at"].items():
+        r, c = map(int, k.split(","))
+        q[r, c] = v
+    w = formats.dequant_fp8_b32(q, np.array(g["scales"], np.uint8), g["rows"], g["cols"])
+    for k, v in g["expected_at"].items():
+        r, c = map(int, k.split(","))
+        assert w[r, c] == v, k
+
+
+def test_worked_mxfp8():
+    g = load("worked_blocks.json")["mxfp8"]
+    q = np.zeros((g["rows"], g["cols"]), np.uint8)
+    for k, v in g["codes_at"].items():
+        r, c = map(int, k.split(","))
+        q[r, c] = v
+    w = formats.dequant_mxfp8(q, np.array(g["scales"], np.uint8), g["rows"], g["cols"])
+    for k, v in g["expected_at"].items():
+        r, c = map(int, k.split(","))
+        assert w[r, c] == v, k
+
+
+def test_fp8_tile_sizes_and_bits_per_weight():
+    t = load("page_figures.json")["fp8_tile_sizes"]
+    H = 4096
+    assert formats.packed_bytes(formats.FP8_B128, H, H) == H * H + (H // t["v4"]) ** 2
+    assert formats.packed_bytes(formats.FP8_B32, H, H) == H * H + (H // t["v4_1"]) ** 2
+    assert formats.packed_bytes(formats.FP8_B32, 4096, 2048) * 8 / (4096 * 2048) == 8 + 8 / 1024
+    # MXFP8: an 8-bit element plus an 8-bit shared scale per 32 elements
+    assert formats.packed_bytes(formats.MXFP8, 2048, 4096) * 8 / (2048 * 4096) == 8.25
+    assert formats.packed_bytes(formats.FP8_B32, 48, 64) == 0       # rows not a multiple of 32
+    assert formats.packed_bytes(formats.MXFP8, 3, 48) == 0          # cols not a multiple of 32
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_roundtrip_mxfp8(seed):
+    rng = np.random.default_rng(40 + seed)
+    rows, cols = 4, 96
+    codes = rng.integers(0, 254, (rows, cols))
+    codes = np.where(codes >= 0x7F, codes + 1, codes)           # skip 0x7f (NaN)
+    E = rng.integers(0, 255, (rows, cols // 32))
+    q, s, exact = enc.encode_mxfp8(codes, E, rows, cols)
+    _assert_exact(formats.dequant_mxfp8(q, s, rows, cols), exact)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_roundtrip_fp8_b32(seed):
+    rng = np.random.default_rng(50 + seed)
+    rows, cols = 64, 96
+    codes = rng.integers(0, 254, (rows, cols))
+    codes = np.where(codes >= 0x7F, codes + 1, codes)
+    S = rng.integers(0, 255, (rows // 32, cols // 32))
+    q, s, exact = enc.encode_fp8_b32(codes, S, rows, cols)
+    w = formats.dequant_fp8_b32(q, s, rows, cols)
+    for r in (0, 31, 32, 63):
+        _assert_exact(w[r:r + 1], [exact[r]])
+
+
+def test_fp8_b32_reduces_to_b128_when_tiles_agree():
+    rng = np.random.default_rng(60)
+    q = rng.integers(0, 0x7F, (256, 256)).astype(np.uint8)
+    S128 = rng.integers(110, 140, (2, 2)).astype(np.uint8)
+    S32 = np.repeat(np.repeat(S128, 4, axis=0), 4, axis=1)
+    assert np.array_equal(formats.dequant_fp8_b32(q, S32, 256, 256), formats.dequant_fp8_b128(q, S128, 256, 256))
+    # the page's hazard: the same scale bytes read with the other tile size rescale weights
+    S32b = rng.integers(110, 140, (8, 8)).astype(np.uint8)
+    as128 = formats.dequant_fp8_b128(q, S32b[:2, :2], 256, 256)
+    assert not np.array_equal(formats.dequant_fp8_b32(q, S32b, 256, 256), as128)
+
+
+def test_mxfp8_equals_fp8_tiles_with_per_row_scales():
+    # an FP8 block-32 tensor is an MXFP8 tensor whose scales repeat over 32 rows
+    rng = np.random.default_rng(61)
+    q = rng.integers(0, 0x7F, (64, 128)).astype(np.uint8)
+    S = rng.integers(100, 150, (2, 4)).astype(np.uint8)
+    E = np.repeat(S, 32, axis=0)
+    assert np.array_equal(formats.dequant_fp8_b32(q, S, 64, 128), formats.dequant_mxfp8(q, E, 64, 128))
+
+
+# ---------------------------------------------------------------- NVFP4 -> MXFP4
+
+@pytest.mark.parametrize("seed", range(4))
+def test_nvfp4_to_mxfp4_inverts_the_forward_conversion(seed):
+    rng = np.random.default_rng(70 + seed)
+    rows, cols = 8, 256
+    nib = rng.integers(0, 256, rows * cols // 2, dtype=np.uint8)
+    lo = int(rng.integers(1, 200))
+    e8 = rng.integers(lo, lo + 18, rows * cols // 32).astype(np.uint8)
+    n2, e4, s2 = convert.mxfp4_to_nvfp4(nib, e8, rows, cols)
+    n3, e8b = convert.nvfp4_to_mxfp4(n2, e4, s2, rows, cols)
+    assert n3.tobytes() == nib.tobytes() and e8b.tobytes() == e8.tobytes()
+    assert np.array_equal(formats.dequant_mxfp4(n3, e8b, rows, cols), formats.dequant_nvfp4(n2, e4, s2, rows, cols))
+
+
+def test_nvfp4_to_mxfp4_refuses_what_e8m0_cannot_hold():
+    nib = np.zeros(16, np.uint8)
+    ok = np.full(2, 0x38, np.uint8)                                  # 1.0 on both halves
+    n, e = convert.nvfp4_to_mxfp4(nib, ok, 0.25, 1, 32)
+    assert e.tolist() == [[125]]                                     # 1.0 * 2^-2
+    for e4, s2 in [(np.array([0x38, 0x40], np.uint8), 1.0),         # halves differ
+                   (np.full(2, 0x3C, np.uint8), 1.0),               # 1.5: not a power of two
+                   (ok, 1.5),                                        # scale_2 not a power of two
+                   (np.zeros(2, np.uint8), 1.0),                     # zero scale
+                   (np.full(2, 0xB8, np.uint8), 1.0),                # negative scale
+                   (ok, 2.0 ** -128)]:                               # below e8m0's range
+        with pytest.raises(convert.LossyConversion):
+            convert.nvfp4_to_mxfp4(nib, e4, s2, 1, 32)
