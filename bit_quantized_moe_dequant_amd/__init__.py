@@ -23,7 +23,9 @@ _LIB_PATH = os.path.join(_HERE, "libmoeq.so")
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "moeq.h")
 
 FMT_MXFP4, FMT_NVFP4, FMT_Q2_K, FMT_IQ2_XXS, FMT_FP8_B128 = 1, 2, 3, 4, 5
-FMT_BY_NAME = {"mxfp4": 1, "nvfp4": 2, "q2_k": 3, "iq2_xxs": 4, "fp8_b128": 5}
+FMT_MXFP8, FMT_FP8_B32, FMT_MXFP8_TILED = 6, 7, 8
+FMT_BY_NAME = {"mxfp4": 1, "nvfp4": 2, "q2_k": 3, "iq2_xxs": 4, "fp8_b128": 5, "mxfp8": 6, "fp8_b32": 7,
+               "mxfp8_tiled": 8}
 
 MOEQ_OK = 0
 MOEQ_E_SCRATCH = -8
@@ -75,6 +77,9 @@ _SIGS = {
     "moeq_quantize_mxfp8": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moeq_quantize_mxfp8_f32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moeq_check_device_error": (_i, [_vp, _vp, ctypes.POINTER(ctypes.c_uint32), _i]),
+    "moeq_mxfp8_to_tiled": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "moeq_mxfp4_to_nvfp4_device": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moeq_nvfp4_to_mxfp4_device": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "moeq_synth_fill": (_i, [_vp, _sz, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, _i, _vp, _vp]),
 }
 
@@ -496,6 +501,59 @@ def mxfp4_to_nvfp4(nib: np.ndarray, e8m0: np.ndarray, rows: int, cols: int):
     _check("moeq_mxfp4_to_nvfp4", _lib().moeq_mxfp4_to_nvfp4(nib.ctypes.data, e8.ctypes.data, rows, cols,
                                                               n2.ctypes.data, e4.ctypes.data, ctypes.byref(s2)))
     return n2, e4, np.float32(s2.value)
+
+
+def mxfp8_to_tiled(data, scales, rows: int, cols: int, n: int = 1, tdata=None, tscales=None):
+    """Row-major MXFP8 planes of n tensors (device uint8) -> the pre-stored operand
+    order (MOEQ_FMT_MXFP8_TILED). Returns (tdata, tscales)."""
+    torch = _torch()
+    _want("data", data, (torch.uint8,), (n * rows * cols,))
+    _want("scales", scales, (torch.uint8,), (n * rows * cols // 32,))
+    if tdata is None:
+        tdata = torch.empty_like(data)
+    if tscales is None:
+        tscales = torch.empty_like(scales)
+    _want("tdata", tdata, (torch.uint8,), tuple(data.shape))
+    _want("tscales", tscales, (torch.uint8,), tuple(scales.shape))
+    _require_cuda(data, scales, tdata, tscales)
+    _check("moeq_mxfp8_to_tiled", _lib().moeq_mxfp8_to_tiled(_ptr(data), _ptr(scales), rows, cols, n, _ptr(tdata),
+                                                              _ptr(tscales), _stream_ptr()))
+    return tdata, tscales
+
+
+def mxfp4_to_nvfp4_device(nib, e8m0, rows: int, cols: int, n: int = 1, nib_out=None):
+    """Device MXFP4 -> NVFP4 re-encode of n tensors. Returns (nibbles, e4m3 codes,
+    scale_2 [n], status [n]); status 1 marks a tensor that cannot be carried
+    exactly (its outputs are not written)."""
+    torch = _torch()
+    _want("nib", nib, (torch.uint8,), (n * rows * cols // 2,))
+    _want("e8m0", e8m0, (torch.uint8,), (n * rows * cols // 32,))
+    if nib_out is None:
+        nib_out = torch.zeros_like(nib)
+    e4 = torch.zeros(n * rows * cols // 16, dtype=torch.uint8, device=nib.device)
+    s2 = torch.zeros(n, dtype=torch.float32, device=nib.device)
+    st = torch.full((n,), 7, dtype=torch.int32, device=nib.device)
+    _require_cuda(nib, e8m0, nib_out)
+    _check("moeq_mxfp4_to_nvfp4_device", _lib().moeq_mxfp4_to_nvfp4_device(
+        _ptr(nib), _ptr(e8m0), rows, cols, n, _ptr(nib_out), _ptr(e4), _ptr(s2), _ptr(st), _stream_ptr()))
+    return nib_out, e4, s2, st
+
+
+def nvfp4_to_mxfp4_device(nib, e4m3, scale2, rows: int, cols: int, n: int = 1, nib_out=None):
+    """Device NVFP4 -> MXFP4 re-encode of n tensors. Returns (nibbles, e8m0 codes,
+    status [n])."""
+    torch = _torch()
+    _want("nib", nib, (torch.uint8,), (n * rows * cols // 2,))
+    _want("e4m3", e4m3, (torch.uint8,), (n * rows * cols // 16,))
+    _want("scale2", scale2, (torch.float32,), (n,))
+    if nib_out is None:
+        nib_out = torch.zeros_like(nib)
+    e8 = torch.zeros(n * rows * cols // 32, dtype=torch.uint8, device=nib.device)
+    st = torch.full((n,), 7, dtype=torch.int32, device=nib.device)
+    _require_cuda(nib, e4m3, scale2, nib_out)
+    _check("moeq_nvfp4_to_mxfp4_device", _lib().moeq_nvfp4_to_mxfp4_device(
+        _ptr(nib), _ptr(e4m3), _ptr(scale2), rows, cols, n, _ptr(nib_out), _ptr(e8), _ptr(st), _stream_ptr()))
+    return nib_out, e8, st
 
 
 def synth_fill(dst, seed: int, stream: int, byte_offset: int, field: int, d_table=None):

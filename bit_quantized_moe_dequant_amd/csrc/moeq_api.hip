@@ -26,9 +26,15 @@ int block_k(int fmt) {
     case MOEQ_FMT_Q2_K: return 256;
     case MOEQ_FMT_IQ2_XXS: return 256;
     case MOEQ_FMT_FP8_B128: return 128;
+    case MOEQ_FMT_MXFP8: return 32;
+    case MOEQ_FMT_FP8_B32: return 32;
+    case MOEQ_FMT_MXFP8_TILED: return 512;
   }
   return 0;
 }
+
+// Formats for dense linears only (moeq_linear, moeq_dequant), not for layers.
+bool dense_only(int fmt) { return fmt == MOEQ_FMT_MXFP8 || fmt == MOEQ_FMT_FP8_B32 || fmt == MOEQ_FMT_MXFP8_TILED; }
 
 size_t plane_bytes(int fmt, int rows, int cols, int plane) {
   int bk = block_k(fmt);
@@ -42,6 +48,13 @@ size_t plane_bytes(int fmt, int rows, int cols, int plane) {
     case MOEQ_FMT_FP8_B128:
       if (rows % 128) return 0;
       return plane == 0 ? n : (size_t)(rows / 128) * (cols / 128);
+    case MOEQ_FMT_FP8_B32:
+      if (rows % 32) return 0;
+      return plane == 0 ? n : (size_t)(rows / 32) * (cols / 32);
+    case MOEQ_FMT_MXFP8: return plane == 0 ? n : n / 32;
+    case MOEQ_FMT_MXFP8_TILED:
+      if (rows % 16) return 0;
+      return plane == 0 ? n : n / 32;
   }
   return 0;
 }
@@ -90,6 +103,7 @@ int check_layer(const moeq_layer* L) {
   if (L->up.rows != L->inter || L->up.cols != L->hidden) return MOEQ_E_SHAPE;
   if (L->down.rows != L->hidden || L->down.cols != L->inter) return MOEQ_E_SHAPE;
   if (L->gate.fmt != L->up.fmt) return MOEQ_E_FMT;
+  if (dense_only(L->gate.fmt) || dense_only(L->down.fmt)) return MOEQ_E_FMT;
   if (L->gate.n_experts < L->n_experts || L->up.n_experts < L->n_experts || L->down.n_experts < L->n_experts)
     return MOEQ_E_INVAL;
   // h is read as fp32 in 16-byte pieces; x as bf16 in 16-byte pieces
@@ -438,6 +452,34 @@ int moeq_mxfp4_to_nvfp4(const uint8_t* nib_host, const uint8_t* e8m0_host, int r
   return MOEQ_OK;
 }
 
+int moeq_mxfp8_to_tiled(const void* data, const void* scales, int rows, int cols, int n, void* tdata, void* tscales,
+                        void* stream) {
+  if (!data || !scales || !tdata || !tscales || n < 0) return MOEQ_E_INVAL;
+  if (plane_bytes(MOEQ_FMT_MXFP8_TILED, rows, cols, 0) == 0) return MOEQ_E_SHAPE;
+  if (!aligned(data, 16) || !aligned(tdata, 16) || !aligned(tscales, 4)) return MOEQ_E_ALIGN;
+  if (n == 0) return MOEQ_OK;
+  return hip_rc(launch_mxfp8_tile((const uint8_t*)data, (const uint8_t*)scales, rows, cols, n, (uint8_t*)tdata,
+                                  (uint8_t*)tscales, S(stream)));
+}
+
+int moeq_mxfp4_to_nvfp4_device(const uint8_t* nib, const uint8_t* e8m0, int rows, int cols, int n, uint8_t* nib_out,
+                               uint8_t* e4m3_out, float* scale2_out, uint32_t* status, void* stream) {
+  if (!nib || !e8m0 || !nib_out || !e4m3_out || !scale2_out || !status || n < 0) return MOEQ_E_INVAL;
+  if (rows <= 0 || cols <= 0 || cols % 32) return MOEQ_E_SHAPE;
+  if (!aligned(nib, 16) || !aligned(nib_out, 16) || !aligned(scale2_out, 4) || !aligned(status, 4)) return MOEQ_E_ALIGN;
+  if (n == 0) return MOEQ_OK;
+  return hip_rc(launch_mx4_to_nv4(nib, e8m0, rows, cols, n, nib_out, e4m3_out, scale2_out, status, S(stream)));
+}
+
+int moeq_nvfp4_to_mxfp4_device(const uint8_t* nib, const uint8_t* e4m3, const float* scale2, int rows, int cols, int n,
+                               uint8_t* nib_out, uint8_t* e8m0_out, uint32_t* status, void* stream) {
+  if (!nib || !e4m3 || !scale2 || !nib_out || !e8m0_out || !status || n < 0) return MOEQ_E_INVAL;
+  if (rows <= 0 || cols <= 0 || cols % 32) return MOEQ_E_SHAPE;
+  if (!aligned(nib, 16) || !aligned(nib_out, 16) || !aligned(scale2, 4) || !aligned(status, 4)) return MOEQ_E_ALIGN;
+  if (n == 0) return MOEQ_OK;
+  return hip_rc(launch_nv4_to_mx4(nib, e4m3, scale2, rows, cols, n, nib_out, e8m0_out, status, S(stream)));
+}
+
 int moeq_dequant(const moeq_weight* w, int expert, float* out, void* stream) {
   int rc = check_weight(w, false);
   if (rc) return rc;
@@ -585,13 +627,26 @@ int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs,
 int moeq_linear(const moeq_weight* w, int expert, const void* x, int T, float* y, void* stream) {
   int rc = check_weight(w, false);
   if (rc) return rc;
+  const bool mx8 = dense_only(w->fmt);
+  if (mx8 && !linear_mx8_fits(w->fmt, w->rows, w->cols)) return MOEQ_E_SHAPE;
   const bool mfma = w->fmt == MOEQ_FMT_FP8_B128 && T > 1 && linear_fp8_fits(w->rows, w->cols);
   int lpr, cpl;
-  if (!mfma && !chunk_geometry(w->fmt, w->cols, &lpr, &cpl)) return MOEQ_E_SHAPE;
+  if (!mx8 && !mfma && !chunk_geometry(w->fmt, w->cols, &lpr, &cpl)) return MOEQ_E_SHAPE;
   if (expert < 0 || expert >= w->n_experts || T < 0 || !x || !y) return MOEQ_E_INVAL;
   if (!aligned(x, 16) || !aligned(y, 4)) return MOEQ_E_ALIGN;
   if (w->cols % 8) return MOEQ_E_SHAPE;
   if (T == 0) return MOEQ_OK;
+  if (mx8) {
+    Mx8Params mp;
+    mp.w = static_cast<const uint8_t*>(w->data) + (size_t)expert * w->expert_stride;
+    mp.s = static_cast<const uint8_t*>(w->scales) + (size_t)expert * w->scale_expert_stride;
+    mp.x = static_cast<const uint16_t*>(x);
+    mp.y = y;
+    mp.rows = w->rows;
+    mp.cols = w->cols;
+    mp.T = T;
+    return hip_rc(launch_linear_mx8(w->fmt, mp, S(stream)));
+  }
   if (mfma) {
     LinearParams lp;
     lp.w = static_cast<const uint8_t*>(w->data) + (size_t)expert * w->expert_stride;

@@ -19,7 +19,16 @@
 
 namespace moeq {
 
-enum { FMT_MXFP4 = 1, FMT_NVFP4 = 2, FMT_Q2_K = 3, FMT_IQ2_XXS = 4, FMT_FP8_B128 = 5 };
+enum {
+  FMT_MXFP4 = 1,
+  FMT_NVFP4 = 2,
+  FMT_Q2_K = 3,
+  FMT_IQ2_XXS = 4,
+  FMT_FP8_B128 = 5,
+  FMT_MXFP8 = 6,
+  FMT_FP8_B32 = 7,
+  FMT_MXFP8_TILED = 8
+};
 enum { ACT_BF16 = 0, ACT_F32 = 1 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -560,6 +569,90 @@ template <> struct Dec<FMT_FP8_B128> {
   }
   __device__ static int out_col(int ch, int j) { return ch * 16 + j; }
 };
+
+// E4M3 weights with a power-of-two (e8m0) scale: FP8 block-32 (one scale per
+// 32 x 32 tile), MXFP8 (one per 32 along a row) and MXFP8 in the pre-stored
+// matrix-instruction order. Chunk = 16 codes, side = the e8m0 code of its scale.
+// The pre-stored order keeps, per tile of 16 rows x 128 columns, lane L = n + 16g
+// of the 16x16x128 block-scaled instruction together: 32 bytes (row n, columns
+// 16g + [0, 16) then 64 + 16g + [0, 16) of the tile) at tile * 2048 + 32 L; and
+// per 16 rows x 512 columns, the lane's four scale bytes (row n, 32-blocks
+// 4j + g of the four 128-column tiles j) at 256 * group + 4 L.
+template <int FMT> struct DecFp8 {
+  static constexpr int WPC = 16;
+  typedef uint32_t Side;
+  __device__ static Side side(const WView& w, int r, int ch) {
+    const int b = ch >> 1;  // the chunk's 32-block along the row
+    if (FMT == FMT_FP8_B32) return w.scales[(size_t)(r >> 5) * (w.cols / 32) + b];
+    if (FMT == FMT_MXFP8) return w.scales[(size_t)r * (w.cols / 32) + b];
+    // tiled: 16-row tile rt, 512-column group b / 16, step j = (b / 4) % 4, g = b % 4
+    const size_t grp = (size_t)(r >> 4) * (w.cols / 512) + (b >> 4);
+    return w.scales[grp * 256 + 4 * ((r & 15) + 16 * (b & 3)) + ((b >> 2) & 3)];
+  }
+  __device__ static const uint8_t* chunk_ptr(const WView& w, int r, int ch) {
+    if (FMT != FMT_MXFP8_TILED) return w.data + (size_t)r * w.cols + (size_t)ch * 16;
+    const int kt = ch >> 3, p = ch & 7;  // 128-column tile, 16-byte piece within it
+    const size_t tile = (size_t)(r >> 4) * (w.cols / 128) + kt;
+    return w.data + tile * 2048 + 32 * ((r & 15) + 16 * (p & 3)) + 16 * (p >> 2);
+  }
+  template <int ACT>
+  __device__ static void fetch_x(const void* row, int ch, u32x4* raw) {
+    Act<ACT>::template fetch<16>(row, ch * 16, raw);
+  }
+  template <int ACT>
+  __device__ static void prep_x(const u32x4* raw, uint32_t* x, float*) {
+    Act<ACT>::template from_raw<16>(raw, x);
+  }
+  template <int ACT>
+  __device__ static void load_x(const void* row, int ch, uint32_t* x, float*) {
+    Act<ACT>::template load<16>(row, ch * 16, x);
+  }
+  template <int ACT>
+  __device__ static float dot(u32x4 q, Side s, const uint32_t* x, const float*, float acc, const Iq2Lds*) {
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      p = dotp<ACT, 16>(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i], 1.0f, false)), x,
+                        2 * i, p);
+      p = dotp<ACT, 16>(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i], 1.0f, true)), x,
+                        2 * i + 1, p);
+    }
+    return __builtin_fmaf(p, e8m0_f32(s), acc);
+  }
+  __device__ static void to_f32(u32x4 q, Side s, float, const uint8_t*, float* out) {
+    int ex = (int)s - 127;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q[i], 1.0f, false);
+      f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q[i], 1.0f, true);
+      out[4 * i + 0] = __builtin_ldexpf(a.x, ex);
+      out[4 * i + 1] = __builtin_ldexpf(a.y, ex);
+      out[4 * i + 2] = __builtin_ldexpf(b.x, ex);
+      out[4 * i + 3] = __builtin_ldexpf(b.y, ex);
+    }
+    if (s == 255u) {
+#pragma unroll
+      for (int j = 0; j < 16; j++) out[j] = __builtin_nanf("");
+    }
+  }
+  __device__ static int out_col(int ch, int j) { return ch * 16 + j; }
+};
+template <> struct Dec<FMT_MXFP8> : DecFp8<FMT_MXFP8> {};
+template <> struct Dec<FMT_FP8_B32> : DecFp8<FMT_FP8_B32> {};
+template <> struct Dec<FMT_MXFP8_TILED> : DecFp8<FMT_MXFP8_TILED> {};
+
+// e8m0 exponent of a 32-block with maximum a: the smallest 2^e with a / 2^e <= 448
+// (e = p - 9 if the frexp mantissa of a is <= 0.875, else p - 8), clamped to the
+// code range; zero or subnormal maxima give 0.
+__device__ __forceinline__ uint32_t mx_block_exponent(float amax) {
+  const uint32_t ab = f2u(amax);
+  if (ab < 0x00800000u) return 0u;
+  const int p = (int)(ab >> 23) - 126;
+  const uint32_t frac = ab & 0x007FFFFFu;
+  const int e = (frac <= 0x00600000u) ? p - 9 : p - 8;
+  const int E = e + 127;
+  return (uint32_t)(E < 0 ? 0 : (E > 254 ? 254 : E));
+}
 
 // Registers of one chunk's activation slice for a format and activation kind.
 // 16-byte loads behind one chunk's activation slice (fetch_x / prep_x).

@@ -378,6 +378,9 @@ int weights_per_chunk(int fmt) {
     case FMT_Q2_K: return 64;
     case FMT_IQ2_XXS: return 64;
     case FMT_FP8_B128: return 16;
+    case FMT_MXFP8: return 16;
+    case FMT_FP8_B32: return 16;
+    case FMT_MXFP8_TILED: return 16;
   }
   return 0;
 }
@@ -412,6 +415,13 @@ hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int 
       break;
     case FMT_FP8_B128:
       hipLaunchKernelGGL(k_dequant<FMT_FP8_B128>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out);
+      break;
+    case FMT_MXFP8: hipLaunchKernelGGL(k_dequant<FMT_MXFP8>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out); break;
+    case FMT_FP8_B32:
+      hipLaunchKernelGGL(k_dequant<FMT_FP8_B32>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out);
+      break;
+    case FMT_MXFP8_TILED:
+      hipLaunchKernelGGL(k_dequant<FMT_MXFP8_TILED>, grid_dim, blk, 0, s, w, grid, rows, cols, expert, out);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -93,6 +93,16 @@ struct LinearParams {
   int rows, cols, T;
 };
 
+// Dense FP8 linear with power-of-two block scales on the block-scaled matrix
+// instruction (MXFP8, MXFP8 pre-stored in the operand order, FP8 block-32).
+struct Mx8Params {
+  const uint8_t* w;   // E4M3 codes of one expert (row-major, or the pre-stored order)
+  const uint8_t* s;   // its e8m0 scale plane
+  const uint16_t* x;  // bf16 [T][cols], 16-byte aligned
+  float* y;           // fp32 [T][rows]
+  int rows, cols, T;
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_dequant(int fmt, const WeightRef& w, const uint8_t* grid, int rows, int cols, int expert, float* out,
                           hipStream_t s);
@@ -126,6 +136,17 @@ bool gu_iq2_fits(int rows, int cols);  // cols % 256 == 0
 hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, bool wide, hipStream_t s);
 bool linear_fp8_fits(int rows, int cols);  // rows % 128 == 0, cols % 256 == 0
 hipError_t launch_linear_fp8(const LinearParams& p, hipStream_t s);
+
+bool linear_mx8_fits(int fmt, int rows, int cols);  // rows % 16, cols % 128 (pre-stored: % 512), cols <= 8192
+hipError_t launch_linear_mx8(int fmt, const Mx8Params& p, hipStream_t s);
+// Row-major MXFP8 -> the pre-stored operand order, n tensors back to back.
+hipError_t launch_mxfp8_tile(const uint8_t* data, const uint8_t* scales, int rows, int cols, int n, uint8_t* tdata,
+                             uint8_t* tscales, hipStream_t s);
+// MXFP4 <-> NVFP4 scale re-encodes of n tensors back to back (status[i] = 1: not exact, outputs untouched).
+hipError_t launch_mx4_to_nv4(const uint8_t* nib, const uint8_t* e8m0, int rows, int cols, int n, uint8_t* nib_out,
+                             uint8_t* e4m3_out, float* scale2_out, uint32_t* status, hipStream_t s);
+hipError_t launch_nv4_to_mx4(const uint8_t* nib, const uint8_t* e4m3, const float* scale2, int rows, int cols, int n,
+                             uint8_t* nib_out, uint8_t* e8m0_out, uint32_t* status, hipStream_t s);
 
 // Chunk geometry: weights per 16-byte chunk; lanes per row and chunks per lane.
 int weights_per_chunk(int fmt);

@@ -83,12 +83,35 @@ extern "C" {
  * MOEQ_FMT_FP8_B128 - E4M3 weights with one UE8M0 scale per 128x128 tile (IQ2_XXS
  *   + Q2_K + FP8 hybrid card, format table; W4A16-FP8 card, FP8 block 128x128).
  *   data: u8 [rows][cols] e4m3fn codes. scales: u8 [rows/128][cols/128].
+ *
+ * Dense-linear formats (moeq_linear and moeq_dequant only; a layer using one is
+ * refused with MOEQ_E_FMT):
+ * MOEQ_FMT_FP8_B32 - E4M3 weights with one UE8M0 scale per 32x32 tile, the dense
+ *   FP8 weights of DeepSeek-V4.1 (DeepSeek-V4.1-Flash mixed-Q2 GGUF card, Recipe:
+ *   V4.1 uses 32x32 E8M0 block scales, V4 128x128; reading one as the other
+ *   rescales every weight). data: u8 [rows][cols]; scales: u8 [rows/32][cols/32].
+ * MOEQ_FMT_MXFP8 - E4M3 elements with one e8m0 scale per 32 along cols (8.25 bits
+ *   per weight), the checkpoint's format for attention, shared experts and the head
+ *   (DeepSeekv4 Flash for 1x Spark forum thread, first post).
+ *   data: u8 [rows][cols]; scales: u8 [rows][cols/32]; weight = e4m3 * 2^(E-127).
+ * MOEQ_FMT_MXFP8_TILED - the same bytes pre-stored in the order of the block-scaled
+ *   matrix instruction's operand (same thread, second post: MXFP8 weights stored
+ *   in the matrix engine's layout so that nothing is repacked at run time); rows a
+ *   multiple of 16, cols of 512. Made from MOEQ_FMT_MXFP8 by moeq_mxfp8_to_tiled.
+ *   data: per tile of 16 rows x 128 cols (tile = (r/16) * (cols/128) + c/128),
+ *   2048 bytes at tile * 2048; lane L = n + 16g of the tile holds the 32 bytes at
+ *   32 L: row n, cols 16g + [0, 16) then 64 + 16g + [0, 16) of the tile.
+ *   scales: per group of 16 rows x 512 cols (group = (r/16) * (cols/512) +
+ *   c/512), 256 bytes; byte 4 L + j = e8m0 of row n, 32-block 4j + g of the group.
  */
 #define MOEQ_FMT_MXFP4 1
 #define MOEQ_FMT_NVFP4 2
 #define MOEQ_FMT_Q2_K 3
 #define MOEQ_FMT_IQ2_XXS 4
 #define MOEQ_FMT_FP8_B128 5
+#define MOEQ_FMT_MXFP8 6
+#define MOEQ_FMT_FP8_B32 7
+#define MOEQ_FMT_MXFP8_TILED 8
 
 /* ------------------------------------------------------------------ status */
 #define MOEQ_OK 0
@@ -157,6 +180,31 @@ int moeq_pack_ggml_device(int fmt, const void* blocks, int rows, int cols, int n
  * MOEQ_E_LOSSY if Emax - Emin > 17 or a code is 255; outputs are then untouched. */
 int moeq_mxfp4_to_nvfp4(const uint8_t* nib_host, const uint8_t* e8m0_host, int rows, int cols, uint8_t* nib_out_host,
                         uint8_t* e4m3_out_host, float* scale2_out_host);
+
+/* Row-major MXFP8 (MOEQ_FMT_MXFP8) -> the pre-stored operand order
+ * (MOEQ_FMT_MXFP8_TILED) for n tensors stored back to back in device memory
+ * (data planes rows * cols bytes apart, scale planes rows * cols / 32). rows a
+ * multiple of 16 and cols of 512 (MOEQ_E_SHAPE otherwise); data and tdata 16-byte
+ * aligned, tscales 4-byte aligned; outputs must not overlap inputs. Asynchronous
+ * on `stream`. */
+int moeq_mxfp8_to_tiled(const void* data, const void* scales, int rows, int cols, int n, void* tdata, void* tscales,
+                        void* stream);
+
+/* Device versions of the MXFP4 <-> NVFP4 re-encodes (REAP K180 Mixed NVFP4 card,
+ * conversion section and "How It Was Built" step 3; the rule is the host one above),
+ * for n tensors [rows][cols] stored back to back in device memory: nibbles rows *
+ * cols / 2 bytes apart, e8m0 planes rows * cols / 32, e4m3 planes rows * cols / 16,
+ * one scale_2 per tensor. status (device, u32 [n]) receives 0 for a tensor
+ * converted exactly and 1 for one that cannot be (MXFP4 -> NVFP4: exponent span
+ * above 17 or a NaN scale; NVFP4 -> MXFP4: the two 16-halves of a block differ or
+ * their scale times scale_2 is not a power of two 2^k, -127 <= k <= 127), whose
+ * outputs are then left untouched. nib_out may equal nib (converted in place);
+ * the scale planes must not overlap. Nibble planes 16-byte aligned. Asynchronous on
+ * `stream`. */
+int moeq_mxfp4_to_nvfp4_device(const uint8_t* nib, const uint8_t* e8m0, int rows, int cols, int n, uint8_t* nib_out,
+                               uint8_t* e4m3_out, float* scale2_out, uint32_t* status, void* stream);
+int moeq_nvfp4_to_mxfp4_device(const uint8_t* nib, const uint8_t* e4m3, const float* scale2, int rows, int cols, int n,
+                               uint8_t* nib_out, uint8_t* e8m0_out, uint32_t* status, void* stream);
 
 /* ------------------------------------------------------------------ kernels */
 
@@ -232,6 +280,11 @@ int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs,
 
 /* Dense block-quantized linear y[T][rows] = W_expert x[T][cols] (fp32 out). Any
  * format; FP8_B128 is the dense-layer format (IQ2_XXS + Q2_K + FP8 hybrid card).
+ * MXFP8, MXFP8_TILED and FP8_B32 run on the block-scaled FP8 matrix instruction
+ * for every T (the weights' e8m0 scale is the instruction's scale; x enters as
+ * two E4M3 terms per value with e8m0 scales per 32, exact to 2^-21.8 of each
+ * 32-block's maximum): rows a multiple of 16 (FP8_B32: 32), cols a multiple of
+ * 128 (MXFP8_TILED: 512) and at most 8192, else MOEQ_E_SHAPE.
  * x bf16 [T][cols], 16-byte aligned; y fp32 [T][rows], 4-byte aligned; both
  * caller-owned, y overwritten. FP8_B128 with T >= 2 and cols a multiple of 256
  * runs on the bf16 matrix instruction (E4M3 codes exact in bf16, block scale

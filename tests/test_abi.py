@@ -177,3 +177,28 @@ def test_binding_rejects_wrong_dtypes_and_shapes():
         mq.down(layer, torch.zeros((T, 2, 32), dtype=torch.float32), ids, rw, y=y, ws=ws)
     with pytest.raises(ValueError):
         mq.gate_up(layer, x, ids.to(torch.int64), ws=ws)
+
+
+def test_dense_format_sizes_and_conversion_validation():
+    lib = mq._lib()
+    # plane bytes of the dense-only formats
+    assert mq.plane_bytes(mq.FMT_MXFP8, 48, 640, 0) == 48 * 640 and mq.plane_bytes(mq.FMT_MXFP8, 48, 640, 1) == 960
+    assert mq.plane_bytes(mq.FMT_FP8_B32, 64, 384, 1) == 2 * 12
+    assert mq.plane_bytes(mq.FMT_FP8_B32, 48, 384, 1) == 0                  # rows not a multiple of 32
+    assert mq.plane_bytes(mq.FMT_MXFP8_TILED, 16, 512, 1) == 256
+    assert mq.plane_bytes(mq.FMT_MXFP8_TILED, 16, 640, 0) == 0              # cols not a multiple of 512
+    assert mq.plane_bytes(mq.FMT_MXFP8_TILED, 24, 512, 0) == 0              # rows not a multiple of 16
+    for fmt in (mq.FMT_MXFP8, mq.FMT_FP8_B32, mq.FMT_MXFP8_TILED):
+        assert mq.packed_bytes(fmt, 4096, 4096) == formats.packed_bytes(
+            formats.MXFP8 if fmt != mq.FMT_FP8_B32 else formats.FP8_B32, 4096, 4096)
+    p = ctypes.c_void_p(0x100000)
+    assert lib.moeq_mxfp8_to_tiled(p, p, 16, 640, 1, p, p, None) == -4
+    assert lib.moeq_mxfp8_to_tiled(p, p, 16, 512, -1, p, p, None) == -1
+    assert lib.moeq_mxfp8_to_tiled(p, p, 16, 512, 0, p, p, None) == 0     # nothing to do
+    assert lib.moeq_mxfp4_to_nvfp4_device(p, p, 16, 48, 1, p, p, p, p, None) == -4
+    assert lib.moeq_mxfp4_to_nvfp4_device(p, p, 16, 64, 1, ctypes.c_void_p(0x100008), p, p, p, None) == -3
+    assert lib.moeq_nvfp4_to_mxfp4_device(p, p, p, 16, 64, -2, p, p, p, None) == -1
+    # a layer may not use a dense-only format
+    L = _fake_layer()
+    L.down.fmt = mq.FMT_MXFP8
+    assert lib.moeq_workspace_bytes(ctypes.byref(L), 1) == 0
