@@ -362,6 +362,60 @@ def run_batch(args, wl):
     }), flush=True)
 
 
+def run_dense_linear(args):
+    """A dense FP8 linear (the pages' 4096 x 4096 shared-expert / attention size) in
+    one format, T tokens per step: y = W x with W rotating over 40 stored copies
+    (672 MB, so every step reads its weights from HBM, not from the 256 MB
+    last-level cache). Not the headline metric: prints us per linear and GB/s."""
+    import torch
+
+    import bit_quantized_moe_dequant_amd as mq
+    from bit_quantized_moe_dequant_amd import synth, workloads
+
+    fmt = mq.FMT_BY_NAME[args.fmt]
+    rows = cols = 4096
+    T, K, W = args.tokens, args.steps, args.warmup
+    n_copies = 40
+    log(f"dense linear {args.fmt} {rows}x{cols}, T={T}: building {n_copies} copies")
+    Wt = workloads.build_dense(mq, fmt, 20262, rows, cols, n_copies)
+    x = torch.from_numpy(synth.activations_bf16(20262 + T, T, cols).view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.empty((T, rows), dtype=torch.float32, device="cuda")
+    nbytes = mq.packed_bytes(fmt, rows, cols)
+
+    def step(i):
+        mq.linear(Wt, i % n_copies, x, y=y)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(W + i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / K
+    log(f"{K} linears: {us:.2f} us each")
+    print(json.dumps({
+        "metric": f"dense FP8 linear {rows}x{cols} us per call at T={T} (not the headline)",
+        "value": round(us, 3), "unit": "us", "higher_is_better": False, "steps": K, "warmup": W,
+        "weight_GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 /
+                                                                                  HBM_PEAK_GBS, 2),
+        "weight_bytes": nbytes, "data": "synthetic",
+        "config": {"workload": "dense_linear", "format": args.fmt, "rows": rows, "cols": cols, "tokens": T,
+                   "copies_rotated": n_copies, "launch": "HIP graph of the timed steps"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +424,8 @@ def main():
     ap.add_argument("--workload", default="mxfp4_layer")
     ap.add_argument("--tokens", type=int, default=1,
                     help="decode workloads: tokens per step (T > 1 prints a separate us/layer line)")
+    ap.add_argument("--fmt", default="mxfp8_tiled",
+                    help="dense_linear workload: fp8_b128, fp8_b32, mxfp8 or mxfp8_tiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -395,6 +451,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "copies": 3}))
         return
+    if args.workload == "dense_linear":
+        if args.steps is None:
+            args.steps = 2000
+        return run_dense_linear(args)
     wl = workloads.WORKLOADS[args.workload]
     if args.steps is None:
         args.steps = 100 if wl.prefill else (20 if args.tokens > 1 else 2000)

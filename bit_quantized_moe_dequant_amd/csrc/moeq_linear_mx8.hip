@@ -27,10 +27,13 @@
 // [0, 16) of the 128-wide step; the scale given by lane (., g) covers K-block g;
 // output lane L register r = A row 4(L/16) + r, B column L % 16.
 //
-// Work: one work-group of four waves per 16 weight rows; the waves take
+// Work: one work-group of eight waves per 16 weight rows; the waves take
 // contiguous runs of K steps (a multiple of four steps each) and issue all their
 // weight loads before any arithmetic; the tokens go through LDS eight (four at K
-// above 4096) at a time, and the four waves' partials are added in wave order.
+// above 4096) at a time, all of a pass's token loads issued before its
+// conversion, which runs before the weight loads are issued in the first pass;
+// the eight waves' partials are added in wave order. (Sixteen tokens per pass, two
+// A tiles per step, needed 140 KB of LDS and 200+ registers: slower at every T.)
 #include <hip/hip_runtime.h>
 
 #include "moeq_device.h"
@@ -44,7 +47,7 @@ typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int M8_WAVES = 4;
+constexpr int M8_WAVES = 8;
 constexpr int M8_TOK = 8;          // tokens per pass (A rows = token x term)
 constexpr int M8_STAGE = 32768;    // staged x bytes per term per pass (tokens x K)
 
@@ -89,12 +92,18 @@ __device__ __forceinline__ void bf16_terms(u32x4 v0, u32x4 v1, uint32_t (&w)[2][
   }
 }
 
+#ifndef MOEQ_MX8_XFIRST
+#define MOEQ_MX8_XFIRST 1
+#endif
+
 template <int FMT, int STEPS>
 __global__ __launch_bounds__(64 * M8_WAVES) void k_linear_mx8(Mx8Params P) {
   __shared__ uint8_t code[2][M8_STAGE];
   __shared__ uint8_t sc[2][M8_STAGE / 32];
   __shared__ float red[M8_WAVES][M8_TOK][16];
   constexpr bool TILED = FMT == FMT_MXFP8_TILED;
+  constexpr int NT = 64 * M8_WAVES;
+  constexpr int XC = M8_STAGE / 16 / NT;  // x chunks of 16 values per thread per pass, at most
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -105,26 +114,52 @@ __global__ __launch_bounds__(64 * M8_WAVES) void k_linear_mx8(Mx8Params P) {
   const int nsteps = K / 128;
   const int cpt = K / 16;                        // 16-value chunks per token
   const int tpp = min(M8_TOK, M8_STAGE / K);     // tokens per pass
+  const int nxc = (tpp * cpt + NT - 1) / NT;     // chunk iterations per pass (uniform)
   const int spw = 4 * ((nsteps + 4 * M8_WAVES - 1) / (4 * M8_WAVES));
   const int s0 = wave * spw;
   const int my = max(0, min(spw, nsteps - s0));  // uniform per wave
 
-  // The first pass's first chunk of x, before the weights (the conversion waits
-  // only for it).
-  u32x4 xv0 = u32x4{0u, 0u, 0u, 0u}, xv1 = xv0;
-  {
-    const int c = threadIdx.x;
-    if (c < min(tpp, P.T) * cpt) {
-      const uint16_t* xr = P.x + (size_t)(c / cpt) * K + (c % cpt) * 16;
-      xv0 = ld16(xr);
-      xv1 = ld16(xr + 8);
+  // Issue every x load of a pass, then convert: one memory round trip per pass.
+  auto stage = [&](int t0) {
+    const int tn = min(tpp, P.T - t0);
+    u32x4 xa[XC], xb[XC];
+#pragma unroll
+    for (int j = 0; j < XC; j++) {
+      xa[j] = u32x4{0u, 0u, 0u, 0u};
+      xb[j] = xa[j];
+      const int c = j * NT + (int)threadIdx.x;
+      if (j < nxc && c < tn * cpt) {
+        const uint16_t* xr = P.x + (size_t)(t0 + c / cpt) * K + (c % cpt) * 16;
+        xa[j] = ld16(xr);
+        xb[j] = ld16(xr + 8);
+      }
     }
-  }
+#pragma unroll
+    for (int j = 0; j < XC; j++) {
+      if (j < nxc) {  // uniform
+        const int c = j * NT + (int)threadIdx.x;
+        uint32_t w[2][4], E[2];
+        bf16_terms(xa[j], xb[j], w, E);
+        if (c < tn * cpt) {
+          const int off = (c / cpt) * K + (c % cpt) * 16;
+#pragma unroll
+          for (int tm = 0; tm < 2; tm++) {
+            *reinterpret_cast<u32x4*>(&code[tm][off]) = u32x4{w[tm][0], w[tm][1], w[tm][2], w[tm][3]};
+            if ((c & 1) == 0) sc[tm][off / 32] = (uint8_t)E[tm];
+          }
+        }
+      }
+    }
+  };
+
+  // The first pass's tokens are converted before (MOEQ_MX8_XFIRST) or while the
+  // weight loads go out.
+  if (MOEQ_MX8_XFIRST) stage(0);
   __builtin_amdgcn_sched_barrier(0);
 
   // Every weight load of the wave (steps past its last re-read that one).
   u32x4 qa[STEPS], qb[STEPS];
-  uint32_t sb[TILED ? STEPS / 4 : STEPS];
+  uint32_t sb[TILED ? (STEPS + 3) / 4 : STEPS];
 #pragma unroll
   for (int i = 0; i < STEPS; i++) {
     const int s = min(s0 + min(i, max(my - 1, 0)), nsteps - 1);
@@ -139,7 +174,7 @@ __global__ __launch_bounds__(64 * M8_WAVES) void k_linear_mx8(Mx8Params P) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < (TILED ? STEPS / 4 : STEPS); i++) {
+  for (int i = 0; i < (TILED ? (STEPS + 3) / 4 : STEPS); i++) {
     if constexpr (TILED) {
       const int grp = min(s0 / 4 + i, nsteps / 4 - 1);
       sb[i] = *reinterpret_cast<const uint32_t*>(P.s + ((size_t)(r0 >> 4) * (K / 512) + grp) * 256 + 4 * lane);
@@ -153,34 +188,14 @@ __global__ __launch_bounds__(64 * M8_WAVES) void k_linear_mx8(Mx8Params P) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if (!MOEQ_MX8_XFIRST) stage(0);
 
   const int tok = n >> 1, term = n & 1;  // this lane's A row
   for (int t0 = 0; t0 < P.T; t0 += tpp) {
     const int tn = min(tpp, P.T - t0);
-    __syncthreads();  // the previous pass has read the staging
-    // x of the pass's tokens -> E4M3 terms and their scales in LDS
-    for (int c0 = 0; c0 < tpp * cpt; c0 += 64 * M8_WAVES) {
-      const int c = c0 + (int)threadIdx.x;
-      const bool live = c < tn * cpt;
-      if (t0 > 0 || c0 > 0) {
-        xv0 = u32x4{0u, 0u, 0u, 0u};
-        xv1 = xv0;
-        if (live) {
-          const uint16_t* xr = P.x + (size_t)(t0 + c / cpt) * K + (c % cpt) * 16;
-          xv0 = ld16(xr);
-          xv1 = ld16(xr + 8);
-        }
-      }
-      uint32_t w[2][4], E[2];
-      bf16_terms(xv0, xv1, w, E);
-      if (live) {
-        const int off = (c / cpt) * K + (c % cpt) * 16;
-#pragma unroll
-        for (int tm = 0; tm < 2; tm++) {
-          *reinterpret_cast<u32x4*>(&code[tm][off]) = u32x4{w[tm][0], w[tm][1], w[tm][2], w[tm][3]};
-          if ((c & 1) == 0) sc[tm][off / 32] = (uint8_t)E[tm];
-        }
-      }
+    if (t0 > 0) {
+      __syncthreads();  // the previous pass has read the staging
+      stage(t0);
     }
     __syncthreads();
 
@@ -252,8 +267,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint8_t* data, const u
 template <int FMT>
 hipError_t go(const Mx8Params& p, hipStream_t s) {
   const dim3 g((unsigned)(p.rows / 16)), b(64 * M8_WAVES);
-  if (p.cols <= 4096) hipLaunchKernelGGL((k_linear_mx8<FMT, 8>), g, b, 0, s, p);
-  else hipLaunchKernelGGL((k_linear_mx8<FMT, 16>), g, b, 0, s, p);
+  if (p.cols <= 4096) hipLaunchKernelGGL((k_linear_mx8<FMT, 4>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((k_linear_mx8<FMT, 8>), g, b, 0, s, p);
   return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ Source layouts produced here (the layouts the formats are published in):
   * Q2_K    u8 [rows, cols/256, 84]: scales[16], qs[64], d fp16, dmin fp16
   * IQ2_XXS u8 [rows, cols/256, 66]: d fp16, then 8 x (u32 a0, u32 a1)
   * FP8-B128 codes u8 [rows, cols], ue8m0 u8 [rows/128, cols/128]
+  * FP8-B32  codes u8 [rows, cols], ue8m0 u8 [rows/32, cols/32]
+  * MXFP8   codes u8 [rows, cols], e8m0 u8 [rows, cols/32]
 """
 from __future__ import annotations
 
@@ -134,9 +136,9 @@ def field_bytes(seed: int, stream: int, kind: int, byte_offset: int, nbytes: int
 # bytes [e * plane_bytes, (e + 1) * plane_bytes) of its stream.
 
 PROJ_GATE, PROJ_UP, PROJ_DOWN, PROJ_LINEAR = 0, 1, 2, 3
-FMT_MXFP4, FMT_NVFP4, FMT_Q2_K, FMT_IQ2_XXS, FMT_FP8_B128 = 1, 2, 3, 4, 5
+FMT_MXFP4, FMT_NVFP4, FMT_Q2_K, FMT_IQ2_XXS, FMT_FP8_B128, FMT_MXFP8, FMT_FP8_B32 = 1, 2, 3, 4, 5, 6, 7
 FMT_NAMES = {FMT_MXFP4: "mxfp4", FMT_NVFP4: "nvfp4", FMT_Q2_K: "q2_k",
-             FMT_IQ2_XXS: "iq2_xxs", FMT_FP8_B128: "fp8_b128"}
+             FMT_IQ2_XXS: "iq2_xxs", FMT_FP8_B128: "fp8_b128", FMT_MXFP8: "mxfp8", FMT_FP8_B32: "fp8_b32"}
 
 
 def stream_id(layer: int, proj: int, plane: int) -> int:
@@ -155,6 +157,10 @@ def source_planes(fmt: int, rows: int, cols: int):
         return [(rows * (cols // 256) * 66, FIELD_IQ2_BLOCK)]
     if fmt == FMT_FP8_B128:
         return [(rows * cols, FIELD_E4M3_FINITE), ((rows // 128) * (cols // 128), FIELD_E8M0_119_123)]
+    if fmt == FMT_FP8_B32:
+        return [(rows * cols, FIELD_E4M3_FINITE), ((rows // 32) * (cols // 32), FIELD_E8M0_119_123)]
+    if fmt == FMT_MXFP8:
+        return [(rows * cols, FIELD_E4M3_FINITE), (rows * cols // 32, FIELD_E8M0_119_123)]
     raise ValueError(fmt)
 
 

@@ -77,6 +77,8 @@ _FIELDS = {
     synth.FMT_MXFP4: [synth.FIELD_RAW, synth.FIELD_E8M0_119_123],
     synth.FMT_NVFP4: [synth.FIELD_RAW, synth.FIELD_E4M3_08_28],
     synth.FMT_FP8_B128: [synth.FIELD_E4M3_FINITE, synth.FIELD_E8M0_119_123],
+    synth.FMT_FP8_B32: [synth.FIELD_E4M3_FINITE, synth.FIELD_E8M0_119_123],
+    synth.FMT_MXFP8: [synth.FIELD_E4M3_FINITE, synth.FIELD_E8M0_119_123],
     synth.FMT_Q2_K: [synth.FIELD_Q2K_BLOCK],
     synth.FMT_IQ2_XXS: [synth.FIELD_IQ2_BLOCK],
 }
@@ -152,8 +154,23 @@ def build_linear(mq, seed: int, rows: int, cols: int, layer: int = 0):
     return fill_weight(mq, spec, synth.PROJ_LINEAR, synth.FMT_FP8_B128, rows, cols, 1)
 
 
-def host_linear_planes(seed: int, rows: int, cols: int, layer: int = 0):
-    return synth.expert_source(seed, layer, synth.PROJ_LINEAR, synth.FMT_FP8_B128, rows, cols, 0)
+def host_linear_planes(seed: int, rows: int, cols: int, layer: int = 0, fmt: int = synth.FMT_FP8_B128,
+                       expert: int = 0):
+    return synth.expert_source(seed, layer, synth.PROJ_LINEAR, fmt, rows, cols, expert)
+
+
+def build_dense(mq, fmt: int, seed: int, rows: int, cols: int, n_copies: int = 1):
+    """A dense FP8 weight with n_copies independent tensors (rotated through by the
+    benchmark so that every launch reads HBM). MXFP8_TILED is filled as row-major
+    MXFP8 and converted to the pre-stored order on the device."""
+    src = synth.FMT_MXFP8 if fmt == mq.FMT_MXFP8_TILED else fmt
+    spec = LayerSpec(cols, rows, n_copies, 1, src, src, seed, 0)
+    W = fill_weight(mq, spec, synth.PROJ_LINEAR, src, rows, cols, n_copies)
+    if fmt != mq.FMT_MXFP8_TILED:
+        return W
+    td, ts = mq.mxfp8_to_tiled(W.data, W.scales, rows, cols, n_copies)
+    return mq.Weight(fmt, rows, cols, n_copies, td, ts, expert_stride=W.expert_stride,
+                     scale_expert_stride=W.scale_expert_stride)
 
 
 def routing(workload: Workload, T: int, step: int = 0):
