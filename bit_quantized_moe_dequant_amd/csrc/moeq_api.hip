@@ -219,6 +219,29 @@ bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >=
 #define MOEQ_DN_Q2K_FROM 2.5
 #endif
 
+// MXFP4 decode at T > 1 on the block-scaled matrix instruction (1), or as GEMVs (0).
+#ifndef MOEQ_MX4_BATCHED
+#define MOEQ_MX4_BATCHED 1
+#endif
+
+// Scale plane read in 16-byte runs by the matrix-instruction kernels.
+bool scales16(const moeq_weight& w) {
+  return aligned(w.scales, 16) && (w.n_experts == 1 || w.scale_expert_stride % 16 == 0);
+}
+
+// An all-MXFP4 layer with at most this many tokens runs the single-token
+// matrix-unit kernels over every (token, slot) pair directly: no routing, no
+// partials and no combine (an expert routed by several tokens is read once per
+// token).
+#ifndef MOEQ_MX4_DIRECT_MAX_T
+#define MOEQ_MX4_DIRECT_MAX_T 32
+#endif
+bool mx4_direct(const moeq_layer* L, int T) {
+  return T >= 1 && T <= MOEQ_MX4_DIRECT_MAX_T && L->gate.fmt == MOEQ_FMT_MXFP4 && L->up.fmt == MOEQ_FMT_MXFP4 &&
+         L->down.fmt == MOEQ_FMT_MXFP4 && gu1_mx4_fits(L->inter, L->hidden) &&
+         down1_mx4_fits(L->hidden, L->inter, L->top_k) && scales16(L->gate) && scales16(L->up) && scales16(L->down);
+}
+
 int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
                 hipStream_t s, const LaunchEvents* ev = nullptr) {
   GemvParams p = gemv_params(L, L->gate, &L->up, ws, lay);
@@ -226,23 +249,27 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
   p.ids = ids;
   p.T = T;
   p.out = h;
-  if (T == 1) {
+  if (T == 1 || mx4_direct(L, T)) {
     p.mode = MODE_DIRECT;
-    return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, L->top_k, 1, s, ev));
+    return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, T * L->top_k, 1, s, ev));
   }
   p.mode = MODE_GROUPED;
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
   if (L->gate.fmt == MOEQ_FMT_IQ2_XXS && gu_iq2_fits(L->inter, L->hidden))
     return hip_rc(launch_gu_iq2(p, slots, (double)T * L->top_k >= MOEQ_IQ2_WIDE_FROM * L->n_experts, s));
+  if (MOEQ_MX4_BATCHED && L->gate.fmt == MOEQ_FMT_MXFP4 && gu_mx4_g_fits(L->inter, L->hidden) && scales16(L->gate) &&
+      scales16(L->up))
+    return hip_rc(launch_gu_mx4_g(p, slots, s));
   return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, grouped_wide(L, T) ? 4 : 1, s, ev));
 }
 
 int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
              const WsLayout& lay, hipStream_t s) {
-  if (T == 1) {
+  if (T == 1 || mx4_direct(L, T)) {
     Down1Params d;
     memset(&d, 0, sizeof(d));
+    d.T = T;
     d.w = ref_of(L->down);
     d.grid = L->down.grid;
     d.rows = L->down.rows;
@@ -270,6 +297,9 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
   if (L->down.fmt == MOEQ_FMT_Q2_K && pairs_per_expert(L, T) >= MOEQ_DN_Q2K_FROM &&
       dn_q2k_fits(L->hidden, L->inter, (long)T * L->top_k))
     rc = hip_rc(launch_dn_q2k(p, slots, s));
+  else if (MOEQ_MX4_BATCHED && L->down.fmt == MOEQ_FMT_MXFP4 && dn_mx4_g_fits(L->hidden, L->inter) &&
+           scales16(L->down))
+    rc = hip_rc(launch_dn_mx4_g(p, slots, s));
   else
     rc = hip_rc(launch_gemv(L->down.fmt, EPI_PARTIAL, p, slots, grouped_wide(L, T) ? 2 : 1, s));
   if (rc) return rc;
@@ -578,7 +608,7 @@ int forward(const moeq_layer* L, const void* x, const int32_t* ids, const float*
             const WsLayout& lay, hipStream_t s) {
   int rc;
   float* h = (float*)((uint8_t*)ws + lay.h);
-  if (T > 1) {
+  if (T > 1 && !mx4_direct(L, T)) {
     rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_of(ws, lay), s));
     if (rc) return rc;
   }

@@ -1,0 +1,348 @@
+// Batched decode of MXFP4 experts on the block-scaled matrix instruction
+// v_mfma_scale_f32_16x16x128_f8f6f4: a few tokens per routed expert, as when N
+// decode sessions are co-scheduled and each step's tokens are grouped by expert
+// (DeepSeekv4 Flash for 1x Spark forum thread, second post, "Next up": one
+// weight sweep over N co-scheduled sessions). Each expert's weights are read
+// once per step and fed to the instruction as they sit in memory (FP4 operand B,
+// e8m0 block scale as the B scale); no weight is decoded on the VALU.
+//
+// The tokens are operand A as E4M3 terms with e8m0 scales per 32, their rows
+// carrying (pair, term) couples:
+//   * gate/up: x (bf16) as two terms; rows 2j, 2j + 1 = pair j of a tile of eight
+//     (the split is exact to 2^-21.8 of each 32-block's maximum);
+//   * down: h (fp32) as three terms; rows 3j .. 3j + 2 = pair j of a tile of five
+//     (about 12 significant bits of h).
+// A pair is a (token, slot) of the routing; the route table (the counting sort of
+// the pairs by expert) gives each work-group its expert and the expert's pairs.
+//
+// Work: a work-group is (routed expert, 16 weight rows), eight waves (gate/up) or
+// four (down) on contiguous runs of K steps; all weight loads of a wave go out after the first tile's
+// activations are converted, stay in registers and serve every tile of the
+// expert's pairs; the waves' partial sums meet in LDS and are added in wave order.
+// Gate/up writes h[pair][row] = silu(g) * u; down writes route-weighted partials
+// [pair][row] for the slot-order combine. The bucket of out-of-range ids writes
+// zeros.
+#include <hip/hip_runtime.h>
+
+#include "moeq_device.h"
+#include "moeq_kernels.h"
+
+namespace moeq {
+
+namespace {
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int GB_WAVES = 4;         // down: four waves of up to eight K steps (K <= 2048 uses four)
+constexpr int GB_NT = 64 * GB_WAVES;
+constexpr int GB_STEPS = 8;
+// The first tile's activations are converted before the weight loads are issued
+// (1) or after (0).
+#ifndef MOEQ_G_XFIRST
+#define MOEQ_G_XFIRST 1
+#endif
+#ifndef MOEQ_GU_G_WAVES
+#define MOEQ_GU_G_WAVES 4
+#endif
+constexpr int GU_WAVES = MOEQ_GU_G_WAVES;  // gate/up waves; their K steps cover K <= 4096
+constexpr int GU_NT = 64 * GU_WAVES;
+constexpr int GU_STEPS = 32 / GU_WAVES;
+constexpr int GU_TILE = 8;           // gate/up pairs per instruction (2 terms each)
+constexpr int GU_KMAX = 4096;
+constexpr int DN_TILE = 5;           // down pairs per instruction (3 terms each)
+constexpr int DN_KMAX = 2048;
+
+// Wave w takes K steps [w spw, (w + 1) spw), spw a multiple of 4 (16-byte runs of
+// scale bytes stay inside the row).
+__device__ __forceinline__ int steps_per_wave(int nsteps, int waves) { return 4 * ((nsteps + 4 * waves - 1) / (4 * waves)); }
+
+struct GuStage {
+  uint8_t code[2][GU_TILE * GU_KMAX];
+  uint8_t sc[2][GU_TILE * GU_KMAX / 32];
+};
+
+__global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
+  __shared__ GuStage st;
+  __shared__ float red[GU_WAVES][2][GU_TILE][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.y;
+  if (slot >= P.route.n_slots()[0]) return;
+  const int e = P.route.slots()[slot];
+  const int pstart = P.route.offsets()[e];
+  const int M = P.route.offsets()[e + 1] - pstart;
+  const int n0 = blockIdx.x * 16;
+  if (e >= P.n_experts) {  // out-of-range ids: their h rows are zero
+    for (int i = threadIdx.x; i < M * 16; i += GU_NT) {
+      const int r = n0 + (i & 15);
+      if (r < P.rows) P.out[(size_t)P.route.perm()[pstart + (i >> 4)] * P.rows + r] = 0.f;
+    }
+    return;
+  }
+  const int K = P.cols;
+  const int nsteps = K / 128;
+  const int cpt = K / 16;
+  const int spw = steps_per_wave(nsteps, GU_WAVES);
+  const int s0 = wave * spw;
+  const int my = max(0, min(spw, nsteps - s0));
+  const int n = lane & 15, g = lane >> 4;
+  const int rn = min(n0 + n, P.rows - 1);
+  constexpr int XC = GU_TILE * GU_KMAX / 16 / GU_NT;  // chunk loads per thread per tile, at most
+
+  // A tile's tokens -> two E4M3 terms in LDS (every load first, then the conversion).
+  auto stage = [&](int m0) {
+    const int tn = min(GU_TILE, M - m0);
+    const int nc = (tn * cpt + GU_NT - 1) / GU_NT;  // uniform
+    u32x4 xa[XC], xb[XC];
+#pragma unroll
+    for (int j = 0; j < XC; j++) {
+      xa[j] = u32x4{0u, 0u, 0u, 0u};
+      xb[j] = xa[j];
+      const int c = j * GU_NT + (int)threadIdx.x;
+      if (j < nc && c < tn * cpt) {
+        const int tok = P.route.perm()[pstart + m0 + c / cpt] / P.top_k;
+        const uint16_t* xr = reinterpret_cast<const uint16_t*>(P.act) + (size_t)tok * K + (c % cpt) * 16;
+        xa[j] = ld16(xr);
+        xb[j] = ld16(xr + 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < XC; j++) {
+      if (j < nc) {
+        const int c = j * GU_NT + (int)threadIdx.x;
+        uint32_t w[2][4], E[2];
+        bf16_terms(xa[j], xb[j], w, E);
+        if (c < tn * cpt) {
+          const int off = (c / cpt) * K + (c % cpt) * 16;
+#pragma unroll
+          for (int tm = 0; tm < 2; tm++) {
+            *reinterpret_cast<u32x4*>(&st.code[tm][off]) = u32x4{w[tm][0], w[tm][1], w[tm][2], w[tm][3]};
+            if ((c & 1) == 0) st.sc[tm][off / 32] = (uint8_t)E[tm];
+          }
+        }
+      }
+    }
+  };
+
+  if (MOEQ_G_XFIRST) stage(0);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 q[2][GU_STEPS];
+  u32x4 sbv4[2][GU_STEPS / 4];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    const uint8_t* wd = P.w[mt].data + (size_t)e * P.w[mt].estride + (size_t)rn * (K / 2);
+    const uint8_t* ws = P.w[mt].scales + (size_t)e * P.w[mt].sestride + (size_t)rn * (K / 32);
+#pragma unroll
+    for (int j = 0; j < GU_STEPS / 4; j++) sbv4[mt][j] = ld16(ws + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
+#pragma unroll
+    for (int i = 0; i < GU_STEPS; i++)
+      q[mt][i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (!MOEQ_G_XFIRST) stage(0);
+
+  const int pj = n >> 1, term = n & 1;  // this lane's A row: pair pj of the tile, its term
+  for (int m0 = 0; m0 < M; m0 += GU_TILE) {
+    const int tn = min(GU_TILE, M - m0);
+    if (m0 > 0) {
+      __syncthreads();  // the previous tile has read the staging and the partials
+      stage(m0);
+    }
+    __syncthreads();
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int i = 0; i < GU_STEPS; i++) {
+      if (i < my) {
+        const int s = s0 + i;
+        u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
+        int sa = 0;
+        if (pj < tn) {
+          const int off = pj * K + 128 * s + 16 * g;
+          a0 = *reinterpret_cast<const u32x4*>(&st.code[term][off]);
+          a1 = *reinterpret_cast<const u32x4*>(&st.code[term][off + 64]);
+          sa = st.sc[term][(pj * K) / 32 + 4 * s + g];
+        }
+        const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+          const i32x8_t bv =
+              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
+          const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
+        }
+      }
+    }
+    // lane (column n, g): registers 0, 1 = pair 2g (its terms), 2, 3 = pair 2g + 1
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+      red[wave][mt][2 * g][n] = acc[mt][0] + acc[mt][1];
+      red[wave][mt][2 * g + 1][n] = acc[mt][2] + acc[mt][3];
+    }
+    __syncthreads();
+    if (threadIdx.x < 16 * GU_TILE) {
+      const int j = threadIdx.x >> 4, col = threadIdx.x & 15;
+      const int r = n0 + col;
+      if (j < tn && r < P.rows) {
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int w = 0; w < GU_WAVES; w++) {
+          gs += red[w][0][j][col];
+          us += red[w][1][j][col];
+        }
+        P.out[(size_t)P.route.perm()[pstart + m0 + j] * P.rows + r] = silu_mul(gs, us);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // unused weight re-reads land before the end
+}
+
+struct DnStage {
+  uint8_t code[3][DN_TILE * DN_KMAX];
+  uint8_t sc[3][DN_TILE * DN_KMAX / 32];
+};
+
+__global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
+  __shared__ DnStage st;
+  __shared__ float red[GB_WAVES][16][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.y;
+  if (slot >= P.route.n_slots()[0]) return;
+  const int e = P.route.slots()[slot];
+  const int pstart = P.route.offsets()[e];
+  const int M = P.route.offsets()[e + 1] - pstart;
+  const int n0 = blockIdx.x * 16;
+  if (e >= P.n_experts) {  // out-of-range ids contribute nothing
+    for (int i = threadIdx.x; i < M * 16; i += GB_NT) {
+      const int r = n0 + (i & 15);
+      if (r < P.rows) P.out[(size_t)P.route.perm()[pstart + (i >> 4)] * P.rows + r] = 0.f;
+    }
+    return;
+  }
+  const int K = P.cols;
+  const int nsteps = K / 128;
+  const int cpt = K / 16;
+  const int spw = steps_per_wave(nsteps, GB_WAVES);
+  const int s0 = wave * spw;
+  const int my = max(0, min(spw, nsteps - s0));
+  const int n = lane & 15, g = lane >> 4;
+  const int rn = min(n0 + n, P.rows - 1);
+  constexpr int XC = (DN_TILE * DN_KMAX / 16 + GB_NT - 1) / GB_NT;
+
+  auto stage = [&](int m0) {
+    const int tn = min(DN_TILE, M - m0);
+    const int nc = (tn * cpt + GB_NT - 1) / GB_NT;  // uniform
+    u32x4 hv[XC][4];
+#pragma unroll
+    for (int j = 0; j < XC; j++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) hv[j][i] = u32x4{0u, 0u, 0u, 0u};
+      const int c = j * GB_NT + (int)threadIdx.x;
+      if (j < nc && c < tn * cpt) {
+        const int pair = P.route.perm()[pstart + m0 + c / cpt];
+        const float* hr = reinterpret_cast<const float*>(P.act) + (size_t)pair * K + (c % cpt) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; i++) hv[j][i] = ld16(hr + 4 * i);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < XC; j++) {
+      if (j < nc) {
+        const int c = j * GB_NT + (int)threadIdx.x;
+        uint32_t w[3][4], E[3];
+        f32_terms3(hv[j], w, E);
+        if (c < tn * cpt) {
+          const int off = (c / cpt) * K + (c % cpt) * 16;
+#pragma unroll
+          for (int tm = 0; tm < 3; tm++) {
+            *reinterpret_cast<u32x4*>(&st.code[tm][off]) = u32x4{w[tm][0], w[tm][1], w[tm][2], w[tm][3]};
+            if ((c & 1) == 0) st.sc[tm][off / 32] = (uint8_t)E[tm];
+          }
+        }
+      }
+    }
+  };
+
+  if (MOEQ_G_XFIRST) stage(0);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 q[GB_STEPS];
+  u32x4 sbv4[GB_STEPS / 4];
+  {
+    const uint8_t* wd = P.w[0].data + (size_t)e * P.w[0].estride + (size_t)rn * (K / 2);
+    const uint8_t* ws = P.w[0].scales + (size_t)e * P.w[0].sestride + (size_t)rn * (K / 32);
+#pragma unroll
+    for (int j = 0; j < GB_STEPS / 4; j++) sbv4[j] = ld16(ws + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
+#pragma unroll
+    for (int i = 0; i < GB_STEPS; i++) q[i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (!MOEQ_G_XFIRST) stage(0);
+
+  const int pj = n / 3, term = n % 3;  // this lane's A row (row 15 unused)
+  for (int m0 = 0; m0 < M; m0 += DN_TILE) {
+    const int tn = min(DN_TILE, M - m0);
+    if (m0 > 0) {
+      __syncthreads();
+      stage(m0);
+    }
+    __syncthreads();
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < GB_STEPS; i++) {
+      if (i < my) {
+        const int s = s0 + i;
+        u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
+        int sa = 0;
+        if (pj < tn) {
+          const int off = pj * K + 128 * s + 16 * g;
+          a0 = *reinterpret_cast<const u32x4*>(&st.code[term][off]);
+          a1 = *reinterpret_cast<const u32x4*>(&st.code[term][off + 64]);
+          sa = st.sc[term][(pj * K) / 32 + 4 * s + g];
+        }
+        const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const i32x8_t bv = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[i], q[i], 0, 1, 2, 3, -1, -1, -1, -1));
+        const int sbv = (int)(sbv4[i >> 2][i & 3] >> (8 * g));
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sbv);
+      }
+    }
+    // lane (column n, g) register r = A row 4g + r
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[wave][4 * g + r][n] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 16 * DN_TILE) {
+      const int j = threadIdx.x >> 4, col = threadIdx.x & 15;
+      const int r = n0 + col;
+      if (j < tn && r < P.rows) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < GB_WAVES; w++) v += (red[w][3 * j][col] + red[w][3 * j + 1][col]) + red[w][3 * j + 2][col];
+        const int pair = P.route.perm()[pstart + m0 + j];
+        P.out[(size_t)pair * P.rows + r] = v * P.rw[pair];
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+}  // namespace
+
+// K a multiple of 512 (16-byte scale runs), at most 4096 (gate/up) or 2048 (down).
+bool gu_mx4_g_fits(int rows, int cols) { return rows > 0 && cols > 0 && cols % 512 == 0 && cols <= GU_KMAX; }
+bool dn_mx4_g_fits(int rows, int cols) { return rows > 0 && cols > 0 && cols % 512 == 0 && cols <= DN_KMAX; }
+
+hipError_t launch_gu_mx4_g(const GemvParams& p, int n_slots, hipStream_t s) {
+  if (!gu_mx4_g_fits(p.rows, p.cols)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gu_mx4_g, dim3((unsigned)((p.rows + 15) / 16), (unsigned)n_slots), dim3(GU_NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dn_mx4_g(const GemvParams& p, int n_slots, hipStream_t s) {
+  if (!dn_mx4_g_fits(p.rows, p.cols)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dn_mx4_g, dim3((unsigned)((p.rows + 15) / 16), (unsigned)n_slots), dim3(GB_NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moeq

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
   // Thread t converts values 16t .. 16t + 15 (two threads per 32-block; K <= 4096 =
   // 16 x 256); threads past K re-read the last 16.
   const int k0 = min(16 * (int)threadIdx.x, K - 16);
-  const uint16_t* xr = reinterpret_cast<const uint16_t*>(P.act) + k0;
+  // slot = pair t * top_k + k: token t's row of x
+  const uint16_t* xr = reinterpret_cast<const uint16_t*>(P.act) + (size_t)(slot / P.top_k) * K + k0;
   const u32x4 v0 = ld16(xr), v1 = ld16(xr + 8);
   __builtin_amdgcn_sched_barrier(0);
   const int n = lane & 15, g = lane >> 4;
@@ -323,7 +324,12 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
   const int n0 = blockIdx.x * 16;
   const int K = P.cols;
   const int nsteps = K / 128;
-  const int e = P.ids[slot];
+  // Token blockIdx.y (one token per grid row: its slots' ids, route weights, h, y).
+  const int32_t* ids = P.ids + (size_t)blockIdx.y * P.top_k;
+  const float* rwt = P.rw + (size_t)blockIdx.y * P.top_k;
+  const float* ht = P.h + (size_t)blockIdx.y * P.top_k * K;
+  float* yt = P.y + (size_t)blockIdx.y * P.rows;
+  const int e = ids[slot];
   const bool ok = e >= 0 && e < P.n_experts;
 
   // h first (the conversion waits only for it): thread t converts values 16t ..
@@ -331,10 +337,10 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
   // the block size is 64 x 2 x top_k threads = top_k x K / 16 for K = 2048).
   const int total = P.top_k * K;
   const int v0i = min(16 * (int)threadIdx.x, total - 16);
-  const float* hp = P.h + v0i;
+  const float* hp = ht + v0i;
   // Route weights before anything else: lane k holds rw[k] for the combine at the
   // end, which would otherwise wait a memory round trip after the last barrier.
-  const float rwv = P.rw[min(lane, P.top_k - 1)];
+  const float rwv = rwt[min(lane, P.top_k - 1)];
   const u32x4 hv0 = ld16(hp), hv1 = ld16(hp + 4), hv2 = ld16(hp + 8), hv3 = ld16(hp + 12);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -435,7 +441,7 @@ __global__ __launch_bounds__(64 * DM_KPARTS * DM_SLOTS) void k_down1_mx4(Down1Pa
       y += pk * u2f(__builtin_amdgcn_readlane(f2u(rwv), k));
     }
     const int r = n0 + (int)threadIdx.x;
-    if (r < P.rows) P.y[r] = y;
+    if (r < P.rows) yt[r] = y;
   }
   if (!ok && blockIdx.x == 0 && lane == 0 && part == 0) atomicOr(P.err, 1u);
 }
@@ -452,7 +458,7 @@ bool down1_mx4_fits(int rows, int cols, int top_k) {
 
 hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s) {
   if (!down1_mx4_fits(p.rows, p.cols, p.top_k)) return hipErrorInvalidValue;
-  dim3 g((unsigned)((p.rows + 15) / 16)), b((unsigned)(64 * DM_KPARTS * p.top_k));
+  dim3 g((unsigned)((p.rows + 15) / 16), (unsigned)(p.T > 1 ? p.T : 1)), b((unsigned)(64 * DM_KPARTS * p.top_k));
   hipLaunchKernelGGL(k_down1_mx4, g, b, 0, s, p);
   return hipGetLastError();
 }

@@ -61,7 +61,8 @@ struct Down1Params {
   WeightRef w;
   const uint8_t* grid;
   int rows, cols, n_experts, lpr, chunks, top_k;
-  const float* h;  // fp32 [top_k][cols]
+  int T;           // tokens (the MXFP4 matrix-unit kernel takes one per grid row; 0 or 1 elsewhere)
+  const float* h;  // fp32 [T][top_k][cols]
   const int32_t* ids;
   const float* rw;
   float* y;
@@ -136,6 +137,13 @@ bool gu_iq2_fits(int rows, int cols);  // cols % 256 == 0
 hipError_t launch_gu_iq2(const GemvParams& p, int n_slots, bool wide, hipStream_t s);
 bool linear_fp8_fits(int rows, int cols);  // rows % 128 == 0, cols % 256 == 0
 hipError_t launch_linear_fp8(const LinearParams& p, hipStream_t s);
+
+// Batched (T > 1) MXFP4 gate/up + SwiGLU and down partials on the block-scaled
+// matrix instruction, each routed expert's weights read once per step.
+bool gu_mx4_g_fits(int rows, int cols);  // cols % 512 == 0, cols <= 4096
+bool dn_mx4_g_fits(int rows, int cols);  // cols % 512 == 0, cols <= 2048
+hipError_t launch_gu_mx4_g(const GemvParams& p, int n_slots, hipStream_t s);
+hipError_t launch_dn_mx4_g(const GemvParams& p, int n_slots, hipStream_t s);
 
 bool linear_mx8_fits(int fmt, int rows, int cols);  // rows % 16, cols % 128 (pre-stored: % 512), cols <= 8192
 hipError_t launch_linear_mx8(int fmt, const Mx8Params& p, hipStream_t s);

@@ -45,52 +45,10 @@ namespace {
 
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int M8_WAVES = 8;
 constexpr int M8_TOK = 8;          // tokens per pass (A rows = token x term)
 constexpr int M8_STAGE = 32768;    // staged x bytes per term per pass (tokens x K)
-
-// Two E4M3 terms of 16 consecutive bf16 values (v0, v1: 8 values each), with the
-// e8m0 scale of their 32-block shared with the neighbouring lane (lane ^ 1 holds
-// the block's other half). All lanes of the wave must call it.
-__device__ __forceinline__ void bf16_terms(u32x4 v0, u32x4 v1, uint32_t (&w)[2][4], uint32_t (&E)[2]) {
-  float x[16];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    x[2 * j] = u2f(v0[j] << 16);
-    x[2 * j + 1] = u2f(v0[j] & 0xFFFF0000u);
-    x[8 + 2 * j] = u2f(v1[j] << 16);
-    x[8 + 2 * j + 1] = u2f(v1[j] & 0xFFFF0000u);
-  }
-#pragma unroll
-  for (int term = 0; term < 2; term++) {
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));
-    E[term] = mx_block_exponent(amax);
-    const float scale = u2f(E[term] << 23);  // the conversions' scale operand: 2^(E - 127)
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const i16x2_t lo =
-          __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[4 * j], x[4 * j + 1], scale, false);
-      const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[4 * j + 2], x[4 * j + 3], scale, true);
-      w[term][j] = (amax == 0.f) ? 0u : __builtin_bit_cast(uint32_t, hi);
-    }
-    if (term == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; j++) {  // residual x - hi, exact in fp32
-        const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[0][j], scale, false);
-        const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[0][j], scale, true);
-        x[4 * j] -= a[0];
-        x[4 * j + 1] -= a[1];
-        x[4 * j + 2] -= b[0];
-        x[4 * j + 3] -= b[1];
-      }
-    }
-  }
-}
 
 #ifndef MOEQ_MX8_XFIRST
 #define MOEQ_MX8_XFIRST 1

@@ -1,0 +1,94 @@
+"""Batched MXFP4 decode (T > 1) on the block-scaled matrix instruction against the
+CPU oracle. Up to 32 tokens the single-token kernels run over every (token, slot)
+pair; beyond, the grouped kernels take each routed expert's pairs in tiles of
+eight (gate/up) and five (down). Cases: experts with several tiles of pairs,
+out-of-range ids on both paths, and the full DeepSeek-V4-Flash-shaped layer at
+16 and 64 tokens (co-scheduled decode sessions)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_dequant_amd as mq
+from bit_quantized_moe_dequant_amd import synth, workloads
+from oracle import moe
+from tests.helpers import TOL, oracle_weight_fn, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def x_tensor(bits):
+    return cuda(bits.view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("T,E,K", [(2, 8, 6), (5, 8, 6), (40, 8, 6), (9, 3, 2), (17, 2, 1), (33, 2, 1), (32, 8, 6)])
+def test_batched_mxfp4_tiles(T, E, K):
+    """T = 40 over 8 experts gives about 30 pairs per expert: four gate/up tiles and
+    six down tiles, the last partial; T = 33, one slot, two experts: gate/up tiles of
+    8 and a last one of 1 or 2; T = 32 is the largest batch of the direct path."""
+    say("batched mxfp4", T, E, K)
+    spec = workloads.LayerSpec(1024, 512, E, K, mq.FMT_MXFP4, mq.FMT_MXFP4, seed=6100 + T + E)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, E, K)
+    x = synth.activations_bf16(spec.seed + 1, T, 1024)
+    ref_y, ref_h = moe.moe_layer(x, ids, rw, oracle_weight_fn(spec))
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    xt, it, rt = x_tensor(x), cuda(ids), cuda(rw)
+    y = mq.expert_forward(layer, xt, it, rt, ws=ws).cpu().numpy()
+    mq.route(layer, it, ws=ws)
+    h = mq.gate_up(layer, xt, it, ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) == 0
+    eh, ey = rel_err(h, ref_h), rel_err(y, ref_y)
+    say("h err", eh, "y err", ey)
+    assert eh < TOL and ey < TOL
+
+
+@pytest.mark.parametrize("T", [12, 40])
+def test_batched_mxfp4_out_of_range_id(T):
+    """T = 12 runs the single-token kernels over every pair, T = 40 the grouped
+    kernels (the out-of-range ids form a bucket of their own there)."""
+    say("batched mxfp4 bad id", T)
+    E, K = 8, 6
+    spec = workloads.LayerSpec(1024, 512, E, K, mq.FMT_MXFP4, mq.FMT_MXFP4, seed=6200)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, E, K)
+    bad = ids.copy()
+    bad[3, 2] = -1
+    bad[7, 5] = E
+    rw0 = rw.copy()
+    rw0[3, 2] = rw0[7, 5] = 0.0
+    ref_y, _ = moe.moe_layer(x := synth.activations_bf16(spec.seed + 1, T, 1024), ids, rw0, oracle_weight_fn(spec))
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    y = mq.expert_forward(layer, x_tensor(x), cuda(bad), cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    assert rel_err(y, ref_y) < TOL
+
+
+@pytest.mark.parametrize("T,sample", [(16, [0, 5, 15]), (64, [0, 31, 63])])
+def test_batched_mxfp4_full_layer(T, sample):
+    say("batched mxfp4 full layer", T)
+    wl = workloads.WORKLOADS["mxfp4_layer"]
+    layer = workloads.build_layer(mq, wl.spec)
+    ids, rw = synth.uniform_routing(wl.spec.seed + 900 + T, T, 256, 6)
+    x = synth.activations_bf16(wl.spec.seed + 901 + T, T, 4096)
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    y = mq.expert_forward(layer, x_tensor(x), cuda(ids), cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) == 0
+    ref, _ = moe.moe_layer(x[sample], ids[sample], rw[sample], oracle_weight_fn(wl.spec))
+    err = rel_err(y[sample], ref)
+    say("err", err)
+    assert err < TOL
+    del layer
+    torch.cuda.empty_cache()
