@@ -111,9 +111,12 @@ int check_layer(const moeq_layer* L) {
   return MOEQ_OK;
 }
 
-bool prefill_path(const moeq_layer* L, int T) {
-  return T >= PREFILL_MIN_T && L->gate.fmt == MOEQ_FMT_MXFP4 && L->up.fmt == MOEQ_FMT_MXFP4 &&
-         L->down.fmt == MOEQ_FMT_MXFP4;
+// From PREFILL_MIN_T tokens each MXFP4 projection (gate/up, down) takes the W4A8
+// grouped GEMM, whatever the format of the other one (a mixed IQ2_XXS / MXFP4
+// layer, DeepSeekv4 Flash for 1x Spark forum thread, second post: one grouped
+// GEMM per projection).
+bool prefill_buffers(const moeq_layer* L, int T) {
+  return T >= PREFILL_MIN_T && (L->gate.fmt == MOEQ_FMT_MXFP4 || L->down.fmt == MOEQ_FMT_MXFP4);
 }
 
 struct WsLayout {
@@ -135,7 +138,7 @@ WsLayout ws_layout(const moeq_layer* L, int T) {
   off += T > 1 ? align_up(P * L->hidden * 4, 256) : 0;
   w.xq = w.xs = w.hq = w.hs = 0;
   w.err = nullptr;
-  if (prefill_path(L, T)) {
+  if (prefill_buffers(L, T)) {
     w.xq = off;
     off += align_up((size_t)T * L->hidden, 256);
     w.xs = off;
@@ -306,13 +309,19 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
   return hip_rc(launch_combine(partial, T, L->top_k, L->hidden, y, s));
 }
 
-int check_prefill(const moeq_layer* L) {
-  if (L->gate.fmt != MOEQ_FMT_MXFP4 || L->up.fmt != MOEQ_FMT_MXFP4 || L->down.fmt != MOEQ_FMT_MXFP4) return MOEQ_E_FMT;
-  // K advances in chunks of 256 and a work-group covers 256 weight rows
+// The W4A8 prefill stage of the gate/up pair (gate_up) or of down: its weights
+// MXFP4, K advancing in chunks of 256 (hidden and inter multiples of 256), scale
+// planes staged in 8-byte pieces.
+int check_prefill(const moeq_layer* L, bool gate_up) {
+  if (gate_up ? (L->gate.fmt != MOEQ_FMT_MXFP4 || L->up.fmt != MOEQ_FMT_MXFP4) : L->down.fmt != MOEQ_FMT_MXFP4)
+    return MOEQ_E_FMT;
   if (L->hidden % 256 || L->inter % 256) return MOEQ_E_SHAPE;
-  // scales are staged in 8-byte pieces
-  for (const moeq_weight* w : {&L->gate, &L->up, &L->down})
-    if (!aligned(w->scales, 8) || w->scale_expert_stride % 8) return MOEQ_E_ALIGN;
+  if (gate_up) {
+    for (const moeq_weight* w : {&L->gate, &L->up})
+      if (!aligned(w->scales, 8) || w->scale_expert_stride % 8) return MOEQ_E_ALIGN;
+  } else if (!aligned(L->down.scales, 8) || L->down.scale_expert_stride % 8) {
+    return MOEQ_E_ALIGN;
+  }
   return MOEQ_OK;
 }
 
@@ -612,16 +621,23 @@ int forward(const moeq_layer* L, const void* x, const int32_t* ids, const float*
     rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_of(ws, lay), s));
     if (rc) return rc;
   }
-  if (prefill_path(L, T) && check_prefill(L) == MOEQ_OK && prefill_a_fits(L, T)) {
-    uint8_t* xq = (uint8_t*)ws + lay.xq;
-    uint8_t* xs = (uint8_t*)ws + lay.xs;
-    uint8_t* hq = (uint8_t*)ws + lay.hq;
-    uint8_t* hs = (uint8_t*)ws + lay.hs;
+  const bool pf = prefill_buffers(L, T) && prefill_a_fits(L, T);
+  const bool gu_pf = pf && check_prefill(L, true) == MOEQ_OK;
+  const bool dn_pf = pf && check_prefill(L, false) == MOEQ_OK;
+  uint8_t* xq = (uint8_t*)ws + lay.xq;
+  uint8_t* xs = (uint8_t*)ws + lay.xs;
+  uint8_t* hq = (uint8_t*)ws + lay.hq;
+  uint8_t* hs = (uint8_t*)ws + lay.hs;
+  if (gu_pf) {  // W4A8: MXFP8 x; fp32 h too when the down projection needs it
     if ((rc = hip_rc(launch_quant_mxfp8(0, x, T, L->hidden, xq, xs, s)))) return rc;
-    if ((rc = run_prefill_gate_up(L, xq, xs, T, nullptr, hq, hs, ws, lay, s))) return rc;
+    if ((rc = run_prefill_gate_up(L, xq, xs, T, dn_pf ? nullptr : h, hq, hs, ws, lay, s))) return rc;
+  } else if ((rc = run_gate_up(L, x, ids, T, h, ws, lay, s))) {
+    return rc;
+  }
+  if (dn_pf) {  // W4A8: MXFP8 h (quantised here when the gate/up produced fp32)
+    if (!gu_pf && (rc = hip_rc(launch_quant_mxfp8(1, h, T * L->top_k, L->inter, hq, hs, s)))) return rc;
     return run_prefill_down(L, hq, hs, rw, T, y, ws, lay, s);
   }
-  if ((rc = run_gate_up(L, x, ids, T, h, ws, lay, s))) return rc;
   return run_down(L, h, ids, rw, T, y, ws, lay, s);
 }
 
@@ -633,7 +649,7 @@ int moeq_prefill_gate_up(const moeq_layer* L, const uint8_t* xq, const uint8_t* 
                          float* h_f32, uint8_t* hq, uint8_t* hs, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;
-  if ((rc = check_prefill(L))) return rc;
+  if ((rc = check_prefill(L, true))) return rc;
   if (T < 0 || !xq || !xs || !ids || !hq || !hs) return MOEQ_E_INVAL;
   if (!aligned(xq, 16) || !aligned(xs, 8) || (h_f32 && !aligned(h_f32, 4))) return MOEQ_E_ALIGN;
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
@@ -645,7 +661,7 @@ int moeq_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs,
                       int T, float* y, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;
-  if ((rc = check_prefill(L))) return rc;
+  if ((rc = check_prefill(L, false))) return rc;
   if (T < 0 || !hq || !hs || !ids || !rw || !y) return MOEQ_E_INVAL;
   if (!aligned(hq, 16) || !aligned(hs, 8) || !aligned(y, 16)) return MOEQ_E_ALIGN;
   if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;

@@ -12,6 +12,8 @@ the host; activations and routing are drawn on the host.
                   4096 x 4096 dense linear
   iq2_q2k_43      IQ2_XXS gate/up + Q2_K down, 43 layers, bs 1 and 64
   prefill_mxfp4   MXFP4 layer, 2048 prompt tokens routed by a hash of the token id
+  iq2_mxfp4       IQ2_XXS gate/up + MXFP4 down (a late layer of the measured-KL mix)
+  mxfp4_iq2       MXFP4 gate/up + IQ2_XXS down (an early layer of the mix)
 """
 from __future__ import annotations
 
@@ -68,6 +70,12 @@ WORKLOADS = {
                           [1, 16], linear=(4096, 4096)),
     "iq2_q2k_43": Workload("iq2_q2k_43", LayerSpec(4096, 2048, 256, 6, synth.FMT_IQ2_XXS, synth.FMT_Q2_K, _seed(3)),
                            [1, 64], n_layers=43),
+    # layers of the measured-KL mix (IQ2_XXS floor, MXFP4 promoted per projection):
+    # MXFP4 on down in late layers, on gate/up in early ones
+    "iq2_mxfp4": Workload("iq2_mxfp4", LayerSpec(4096, 2048, 256, 6, synth.FMT_IQ2_XXS, synth.FMT_MXFP4, _seed(5)),
+                          [1, 2048]),
+    "mxfp4_iq2": Workload("mxfp4_iq2", LayerSpec(4096, 2048, 256, 6, synth.FMT_MXFP4, synth.FMT_IQ2_XXS, _seed(6)),
+                          [1, 2048]),
     "prefill_mxfp4": Workload("prefill_mxfp4",
                               LayerSpec(4096, 2048, 256, 6, synth.FMT_MXFP4, synth.FMT_MXFP4, _seed(4)),
                               [2048], prefill=True),

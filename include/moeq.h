@@ -220,10 +220,14 @@ int moeq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* y[T][H] (fp32, overwritten) of the routed layer for x[T][H] (bf16), expert ids
  * ids[T][K] (int32) and route weights rw[T][K] (fp32, applied after down as given).
- * Decode path (any format: the stage kernels below) unless T >= 128, gate, up
- * and down are all MXFP4 and the layer meets the prefill stages' shape and
- * alignment conditions (below), in which case the W4A8 prefill path runs (x and h
- * quantised to MXFP8). T == 0 is a no-op. x, y 16-byte aligned. */
+ * Decode path (any format: the stage kernels below) below T = 128 tokens. From
+ * T = 128, each MXFP4 projection that meets the prefill stages' shape and
+ * alignment conditions (below) runs the W4A8 prefill GEMM instead (gate/up on x
+ * quantised to MXFP8; down on h quantised to MXFP8), whatever the format of the
+ * other projection: a layer mixing IQ2_XXS (or Q2_K) and MXFP4 projections takes
+ * the W4A8 GEMM for its MXFP4 projection and the grouped decode kernels for the
+ * other (1x Spark forum thread, second post: one grouped GEMM per projection).
+ * T == 0 is a no-op. x, y 16-byte aligned. */
 int moeq_expert_forward(const moeq_layer* L, const void* x, const int32_t* ids, const float* rw, int T, float* y,
                         void* ws, size_t ws_bytes, void* stream);
 
@@ -263,10 +267,10 @@ int moeq_down(const moeq_layer* L, const float* h, const int32_t* ids, const flo
 int moeq_gate_up_timed(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws,
                        size_t ws_bytes, void* stream, void* start_event, void* stop_event);
 
-/* Stages of the W4A8 prefill path (MXFP4 weights only, hidden and inter multiples
- * of 256, weight scale planes and their expert stride 8-byte aligned, else
- * MOEQ_E_ALIGN);
- * moeq_route first, on the same workspace).
+/* Stages of the W4A8 prefill path, one per projection (its weights MXFP4, else
+ * MOEQ_E_FMT; the other projection may be in any format; hidden and inter
+ * multiples of 256; the stage's weight scale planes and their expert stride
+ * 8-byte aligned, else MOEQ_E_ALIGN; moeq_route first, on the same workspace).
  * moeq_prefill_gate_up: xq/xs = MXFP8 x (codes u8 [T][H], 16-byte aligned; e8m0
  *   u8 [T][H/32], 8-byte aligned) -> hq/hs = MXFP8 h (codes u8 [T*K][I], e8m0 u8
  *   [T*K][I/32]); h_f32 (may be NULL) receives h before quantisation, fp32 [T*K][I].

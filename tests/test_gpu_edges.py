@@ -8,7 +8,8 @@
   blocks that each hold one outlier 2^8 .. 2^20 times the other values;
 * the Q2_K down fed an fp32 h with full 24-bit mantissas, at one and sixteen
   tokens, against a bound much tighter than the projection tolerance;
-* full forwards of a layer with IQ2_XXS gate/up and MXFP4 down (mixed formats).
+* full forwards of a layer with IQ2_XXS gate/up and MXFP4 down (mixed formats) at
+  decode sizes.
 
 Every expected value comes from the CPU oracle on the same seeded inputs."""
 import sys
@@ -150,11 +151,13 @@ def test_grouped_2bit_kernels_full_depth():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T,sample", [(16, None), (256, [0, 100, 255])])
+@pytest.mark.parametrize("T,sample", [(16, None), (96, [0, 50, 95])])
 def test_mixed_iq2_gate_up_mxfp4_down_forward(T, sample):
     """A layer whose gate/up is IQ2_XXS and whose down is MXFP4, end to end through
-    moeq_expert_forward (routing, grouped IQ2_XXS gate/up, MXFP4 down partials,
-    combine)."""
+    moeq_expert_forward at decode sizes (routing, grouped IQ2_XXS gate/up, MXFP4
+    down, combine) against the exact layer. From 128 tokens the MXFP4 down takes
+    the W4A8 prefill GEMM instead (MXFP8 h), checked stage by stage in
+    test_gpu_prefill_mixed.py."""
     say("mixed iq2/mxfp4", T)
     spec = workloads.LayerSpec(1024, 512, 32, 6, mq.FMT_IQ2_XXS, mq.FMT_MXFP4, seed=5400 + T)
     layer = workloads.build_layer(mq, spec)
