@@ -300,6 +300,9 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
   if (L->down.fmt == MOEQ_FMT_Q2_K && pairs_per_expert(L, T) >= MOEQ_DN_Q2K_FROM &&
       dn_q2k_fits(L->hidden, L->inter, (long)T * L->top_k))
     rc = hip_rc(launch_dn_q2k(p, slots, s));
+  else if (L->down.fmt == MOEQ_FMT_IQ2_XXS && pairs_per_expert(L, T) >= MOEQ_DN_Q2K_FROM &&
+           dn_q2k_fits(L->hidden, L->inter, (long)T * L->top_k))
+    rc = hip_rc(launch_dn_iq2(p, slots, s));
   else if (MOEQ_MX4_BATCHED && L->down.fmt == MOEQ_FMT_MXFP4 && dn_mx4_g_fits(L->hidden, L->inter) &&
            scales16(L->down))
     rc = hip_rc(launch_dn_mx4_g(p, slots, s));

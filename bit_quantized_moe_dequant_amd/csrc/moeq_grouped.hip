@@ -551,6 +551,161 @@ __global__ __launch_bounds__(64 * GI_WAVES) void k_dn_q2k(GemvParams P) {
   }
 }
 
+// ---------------------------------------------------------------- IQ2_XXS down, token-grouped
+// The down projection of IQ2_XXS experts for batches (T > 1), on
+// v_mfma_f32_16x16x32_bf16, for the layers of the mix whose down projection keeps
+// the IQ2_XXS floor (DeepSeekv4 Flash for 1x Spark forum thread, first post: an
+// IQ2_XXS floor on most experts). As in k_gu_iq2, one instruction covers one
+// 32-weight sub-block of 16 weight rows (operand B, decoded exactly into bf16)
+// and the sub-block scale multiplies the instruction's fp32 partial in the lane
+// that decoded it; the tokens (operand A) are h as bf16 hi + lo pairs (16
+// significant bits, the rounding of the split is the only one besides fp32
+// sums), two instructions per sub-block. The work-group's four waves (64 weight
+// rows) share each 16-token tile's h, staged once per superblock in LDS already in
+// the instruction's operand order; two buffers, one barrier per superblock, loads
+// two superblocks ahead. Outputs are route-weighted partials per (pair, row).
+struct GdStage {
+  u32x4 a[8 * 16 * 4 * 2];  // [((sub-block j * 16 + token m) * 4 + group g) * 2 + lo]: 8 bf16 at K = 32 j + 8 g
+};
+
+struct GdW {
+  u32x4 w[4];  // the superblock's 64 data bytes of row n
+  uint32_t d;  // its fp16 d
+};
+
+__device__ __forceinline__ void gd_wload(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr, int w_off, int s_off,
+                                         int sb, GdW& b) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    b.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off + 16 * i, sb * 64, 0));
+  b.d = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off, sb * 2, 0);
+}
+
+// This thread's (token tm, half hf of sub-block j): 16 fp32 h values (K = 32 j +
+// 16 hf + [0, 16)) -> groups 2 hf and 2 hf + 1 as bf16 hi and lo octets.
+__device__ __forceinline__ void gd_stage_write(const u32x4 (&v)[4], int tm, int j, int hf, GdStage& s) {
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const u32x4 u = v[2 * q + i];
+      split_pair(u2f(u[0]), u2f(u[1]), hi[2 * i], lo[2 * i]);
+      split_pair(u2f(u[2]), u2f(u[3]), hi[2 * i + 1], lo[2 * i + 1]);
+    }
+    const int base = ((j * 16 + tm) * 4 + 2 * hf + q) * 2;
+    s.a[base] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    s.a[base + 1] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  }
+}
+
+__device__ __forceinline__ void gd_compute(const GdW& b, const GdStage& s, int n, int g, const Iq2Lds* t,
+                                           const GiSigns* sg, f32x4_t& acc) {
+  const float d8 = half_bits_f32(b.d) * 0.125f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const uint32_t a0 = b.w[j >> 1][2 * (j & 1)], a1 = b.w[j >> 1][2 * (j & 1) + 1];
+    const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
+    const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
+    const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
+    const u32x4 m = sg->w[code];
+    const u32x4 wv = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
+    const int base = ((j * 16 + n) * 4 + g) * 2;  // A row n = token n
+    f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, s.a[base]),
+                                                        __builtin_bit_cast(bf16x8_t, wv), f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                        0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, s.a[base + 1]),
+                                                __builtin_bit_cast(bf16x8_t, wv), c, 0, 0, 0);
+    const float db = d8 * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
+#pragma unroll
+    for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(c[r], db, acc[r]);
+  }
+}
+
+__global__ __launch_bounds__(64 * GI_WAVES) void k_dn_iq2(GemvParams P) {
+  __shared__ Iq2Lds lds_tab[1];
+  __shared__ GiSigns signs[1];
+  __shared__ GdStage stg[2];
+  __shared__ int s_pair[16];
+  __shared__ float s_rw[16];
+  iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
+  if (threadIdx.x < 128) {
+    uint32_t m[4];
+    iq2_sign_words(threadIdx.x, m);
+    signs[0].w[threadIdx.x] = u32x4{m[0], m[1], m[2], m[3]};
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int slot = blockIdx.y;
+  if (slot >= P.route.n_slots()[0]) return;
+  const int e = P.route.slots()[slot];
+  const int pstart = P.route.offsets()[e];
+  const int M = P.route.offsets()[e + 1] - pstart;
+  const int r0 = blockIdx.x * GI_ROWS;
+  if (r0 >= P.rows || M <= 0) return;  // uniform per work-group: the barriers below are reached by all
+  if (e < 0 || e >= P.n_experts) {
+    for (int m = 0; m < M; m++) {
+      const int pair = P.route.perm()[pstart + m];
+      for (int i = threadIdx.x; i < GI_ROWS; i += 64 * GI_WAVES)
+        if (r0 + i < P.rows) P.out[(size_t)pair * P.rows + r0 + i] = 0.f;
+    }
+    return;
+  }
+
+  const int nsb = P.cols / 256;
+  const int n0 = r0 + wave * 16;
+  const int rn = min(n0 + n, P.rows - 1);
+  const __amdgpu_buffer_rsrc_t wr = gi_buffer(P.w[0].data + (size_t)e * P.w[0].estride);
+  const __amdgpu_buffer_rsrc_t sr = gi_buffer(P.w[0].scales + (size_t)e * P.w[0].sestride);
+  const __amdgpu_buffer_rsrc_t xr = gi_buffer(P.act);
+  const int w_off = rn * nsb * 64, s_off = rn * nsb * 2;
+  // staging: thread = (token tm, sub-block tj / 2, half tj % 2)
+  const int tm = threadIdx.x >> 4, tj = threadIdx.x & 15;
+
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    const int pt = P.route.perm()[pstart + min(m0 + tm, M - 1)];  // tokens past the last repeat it
+    if (tj == 0) {
+      s_pair[tm] = pt;
+      s_rw[tm] = P.rw[pt];
+    }
+    const int x_off = pt * P.cols * 4 + 64 * tj;
+    u32x4 v[2][4];
+    GdW W[2];
+    auto xload = [&](int sb, u32x4(&dst)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, x_off + 16 * i, sb * 1024, 0));
+    };
+    xload(0, v[0]);
+    gd_wload(wr, sr, w_off, s_off, 0, W[0]);
+    xload(min(1, nsb - 1), v[1]);
+    gd_wload(wr, sr, w_off, s_off, min(1, nsb - 1), W[1]);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < nsb; sb += 2) {
+#pragma unroll
+      for (int k = 0; k < 2; k++) {
+        if (sb + k < nsb) {  // uniform
+          gd_stage_write(v[k], tm, tj >> 1, tj & 1, stg[k]);
+          xload(min(sb + k + 2, nsb - 1), v[k]);
+          __syncthreads();
+          gd_compute(W[k], stg[k], n, g, &lds_tab[0], &signs[0], acc);
+          gd_wload(wr, sr, w_off, s_off, min(sb + k + 2, nsb - 1), W[k]);
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the final prefetches are never used
+    if (n0 + n < P.rows) {
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (m0 + 4 * g + r < M) P.out[(size_t)s_pair[4 * g + r] * P.rows + n0 + n] = acc[r] * s_rw[4 * g + r];
+    }
+    __syncthreads();  // the staging buffers and s_pair / s_rw are rewritten by the next tile
+  }
+}
+
 }  // namespace
 
 // Buffer offsets are 32-bit: an expert's data plane and the activations must stay
@@ -578,6 +733,17 @@ hipError_t launch_dn_q2k(const GemvParams& p, int n_slots, hipStream_t s) {
   if (!dn_q2k_fits(p.rows, p.cols, (long)p.T * p.top_k)) return hipErrorInvalidValue;
   dim3 g((unsigned)((p.rows + GI_ROWS - 1) / GI_ROWS), (unsigned)n_slots);
   hipLaunchKernelGGL(k_dn_q2k, g, dim3(64 * GI_WAVES), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moeq
+
+namespace moeq {
+
+hipError_t launch_dn_iq2(const GemvParams& p, int n_slots, hipStream_t s) {
+  if (!dn_q2k_fits(p.rows, p.cols, (long)p.T * p.top_k)) return hipErrorInvalidValue;
+  dim3 g((unsigned)((p.rows + GI_ROWS - 1) / GI_ROWS), (unsigned)n_slots);
+  hipLaunchKernelGGL(k_dn_iq2, g, dim3(64 * GI_WAVES), 0, s, p);
   return hipGetLastError();
 }
 

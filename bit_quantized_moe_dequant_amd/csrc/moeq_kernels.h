@@ -131,6 +131,9 @@ hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s);
 // partials [pairs][rows] for the combine.
 bool dn_q2k_fits(int rows, int cols, long pairs);
 hipError_t launch_dn_q2k(const GemvParams& p, int n_slots, hipStream_t s);
+// Token-grouped IQ2_XXS down (T > 1) on the bf16 matrix instruction (same shape
+// conditions as the Q2_K one).
+hipError_t launch_dn_iq2(const GemvParams& p, int n_slots, hipStream_t s);
 bool gu_iq2_fits(int rows, int cols);  // cols % 256 == 0
 // Grouped gate/up + SwiGLU for IQ2_XXS on the bf16 matrix instruction (T > 1).
 // wide: decode each superblock once for two 16-token tiles (many tokens per expert).

@@ -122,14 +122,16 @@ def test_q2k_down_on_oracle_h_is_tight(T):
     torch.cuda.empty_cache()
 
 
-def test_grouped_2bit_kernels_full_depth():
-    """IQ2_XXS gate/up + Q2_K down at hidden 4096 / intermediate 2048 with 4 experts
-    and top-3: about 75 pairs per expert, so the wide IQ2_XXS kernel decodes each of
-    the 16 superblocks along K once for a 64-token pass and a short second pass, and
-    the grouped Q2_K down runs 8 superblocks along K over five 16-token tiles."""
-    say("grouped 2-bit full depth")
+@pytest.mark.parametrize("fmt_dn", [mq.FMT_Q2_K, mq.FMT_IQ2_XXS])
+def test_grouped_2bit_kernels_full_depth(fmt_dn):
+    """IQ2_XXS gate/up + Q2_K or IQ2_XXS down at hidden 4096 / intermediate 2048
+    with 4 experts and top-3: about 75 pairs per expert, so the wide IQ2_XXS kernel
+    decodes each of the 16 superblocks along K once for a 64-token pass and a short
+    second pass, and the grouped down runs 8 superblocks along K over five 16-token
+    tiles."""
+    say("grouped 2-bit full depth", fmt_dn)
     T = 100
-    spec = workloads.LayerSpec(4096, 2048, 4, 3, mq.FMT_IQ2_XXS, mq.FMT_Q2_K, seed=5300)
+    spec = workloads.LayerSpec(4096, 2048, 4, 3, mq.FMT_IQ2_XXS, fmt_dn, seed=5300 + fmt_dn)
     layer = workloads.build_layer(mq, spec)
     ids, rw = synth.uniform_routing(spec.seed, T, 4, 3)
     loads = np.bincount(ids.reshape(-1), minlength=4)
