@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoeq.so")
 
-SOURCES = ["moeq_api.hip", "moeq_gemv.hip", "moeq_aux.hip", "moeq_prefill.hip", "moeq_linear.hip", "moeq_grouped.hip", "moeq_gu_mx4.hip", "moeq_linear_mx8.hip", "moeq_batched.hip", "moeq_convert.hip", "synth.hip"]
+SOURCES = ["moeq_api.hip", "moeq_gemv.hip", "moeq_aux.hip", "moeq_prefill.hip", "moeq_linear.hip", "moeq_grouped.hip", "moeq_gu_mx4.hip", "moeq_linear_mx8.hip", "moeq_batched.hip", "moeq_convert.hip", "moeq_down_q2k.hip", "synth.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -245,6 +245,18 @@ bool mx4_direct(const moeq_layer* L, int T) {
          down1_mx4_fits(L->hidden, L->inter, L->top_k) && scales16(L->gate) && scales16(L->up) && scales16(L->down);
 }
 
+// A Q2_K down with fewer pairs per touched expert than this runs the single-token
+// block-scaled kernel once per token (a grid row each): every routed expert is read
+// once per (token, slot) pair instead of once, but with no partials, no combine and
+// the matrix instruction instead of the grouped GEMV (0 turns the path off).
+#ifndef MOEQ_Q2K_DIRECT_BELOW
+#define MOEQ_Q2K_DIRECT_BELOW 2.5
+#endif
+bool q2k_direct(const moeq_layer* L, int T, const float* h) {
+  return T >= 1 && L->down.fmt == MOEQ_FMT_Q2_K && pairs_per_expert(L, T) < MOEQ_Q2K_DIRECT_BELOW &&
+         down1_q2k_fits(L->hidden, L->inter, L->top_k) && aligned(h, 16);
+}
+
 int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
                 hipStream_t s, const LaunchEvents* ev = nullptr) {
   GemvParams p = gemv_params(L, L->gate, &L->up, ws, lay);
@@ -269,7 +281,7 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
 
 int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
              const WsLayout& lay, hipStream_t s) {
-  if (T == 1 || mx4_direct(L, T)) {
+  if (T == 1 || mx4_direct(L, T) || q2k_direct(L, T, h)) {
     Down1Params d;
     memset(&d, 0, sizeof(d));
     d.T = T;

@@ -697,37 +697,41 @@ __device__ __forceinline__ void bf16_terms(u32x4 v0, u32x4 v1, uint32_t (&w)[2][
   }
 }
 
-// Three E4M3 terms of 16 consecutive fp32 values (v: 4 loads of 4 values), each
-// term with its e8m0 scale per 32 shared with lane ^ 1; the residual after each
-// term is exact in fp32, so the three terms keep about 12 significant bits (the
-// error of an element is at most 2^-12 of it plus 2^-25.8 of its block's
-// maximum). All lanes of the wave must call it.
-__device__ __forceinline__ void f32_terms3(const u32x4 (&v)[4], uint32_t (&w)[3][4], uint32_t (&E)[3]) {
+// NT E4M3 terms of 16 consecutive fp32 values (v: 4 loads of 4 values), each term
+// with its e8m0 scale per 32 shared with lane ^ 1; the residual after each term is
+// exact in fp32 and each term carries four more significant bits, so three terms
+// keep about 12 (the error of an element is at most 2^-12 of it plus 2^-25.8 of its
+// block's maximum) and four about 16. store(term, codes[4], E) receives each term as
+// soon as it is made. All lanes of the wave must call it.
+template <int NT, class Store>
+__device__ __forceinline__ void f32_terms_each(const u32x4 (&v)[4], Store&& store) {
   float x[16];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) x[4 * i + j] = u2f(v[i][j]);
 #pragma unroll
-  for (int term = 0; term < 3; term++) {
+  for (int term = 0; term < NT; term++) {
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
     amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));
-    E[term] = mx_block_exponent(amax);
-    const float scale = u2f(E[term] << 23);
+    const uint32_t E = mx_block_exponent(amax);
+    const float scale = u2f(E << 23);
+    uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const i16x2_t lo =
           __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[4 * j], x[4 * j + 1], scale, false);
       const i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[4 * j + 2], x[4 * j + 3], scale, true);
-      w[term][j] = (amax == 0.f) ? 0u : __builtin_bit_cast(uint32_t, hi);
+      w[j] = (amax == 0.f) ? 0u : __builtin_bit_cast(uint32_t, hi);
     }
-    if (term < 2) {
+    store(term, w, E);
+    if (term + 1 < NT) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[term][j], scale, false);
-        const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[term][j], scale, true);
+        const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], scale, false);
+        const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], scale, true);
         x[4 * j] -= a[0];
         x[4 * j + 1] -= a[1];
         x[4 * j + 2] -= b[0];
@@ -735,6 +739,17 @@ __device__ __forceinline__ void f32_terms3(const u32x4 (&v)[4], uint32_t (&w)[3]
       }
     }
   }
+}
+template <int NT>
+__device__ __forceinline__ void f32_terms(const u32x4 (&v)[4], uint32_t (&w)[NT][4], uint32_t (&E)[NT]) {
+  f32_terms_each<NT>(v, [&](int t, const uint32_t (&c)[4], uint32_t e) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) w[t][j] = c[j];
+    E[t] = e;
+  });
+}
+__device__ __forceinline__ void f32_terms3(const u32x4 (&v)[4], uint32_t (&w)[3][4], uint32_t (&E)[3]) {
+  f32_terms<3>(v, w, E);
 }
 
 // Registers of one chunk's activation slice for a format and activation kind.

@@ -542,12 +542,18 @@ static hipError_t down1_f(const Down1Params& p, int cpl, dim3 g, dim3 b, hipStre
   return p.top_k <= 8 ? down1_fw<FMT, 8>(p, cpl, g, b, s) : down1_fw<FMT, 16>(p, cpl, g, b, s);
 }
 
+#ifndef MOEQ_Q2K_MFMA
+#define MOEQ_Q2K_MFMA 1
+#endif
 hipError_t launch_down1(int fmt, const Down1Params& p, hipStream_t s) {
   // MXFP4: straight into the matrix unit (16-byte scale runs and h loads need
   // 16-byte aligned scale planes and h).
   if (fmt == FMT_MXFP4 && down1_mx4_fits(p.rows, p.cols, p.top_k) && (uintptr_t)p.w.scales % 16 == 0 &&
       p.w.sestride % 16 == 0 && (uintptr_t)p.h % 16 == 0)
     return launch_down1_mx4(p, s);
+  // Q2_K: the 2-bit codes as FP8 operands of the same instruction (16-byte h loads).
+  if (fmt == FMT_Q2_K && MOEQ_Q2K_MFMA && down1_q2k_fits(p.rows, p.cols, p.top_k) && (uintptr_t)p.h % 16 == 0)
+    return launch_down1_q2k(p, s);
   int lpr, cpl;
   if (!chunk_geometry(fmt, p.cols, &lpr, &cpl)) return hipErrorInvalidValue;
   Down1Params q = p;

@@ -127,6 +127,10 @@ hipError_t launch_gu1_fp4(int fmt, const GemvParams& p, int n_slots, hipStream_t
 bool down1_mx4_fits(int rows, int cols, int top_k);  // cols % 512 == 0, cols <= 2048, top_k <= 8
 // Single-token down + weighted combine for MXFP4 on the block-scaled matrix instruction.
 hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s);
+bool down1_q2k_fits(int rows, int cols, int top_k);  // cols % 256 == 0, cols <= 2048, top_k <= 6
+// Q2_K down + weighted combine of one token per grid row (p.T rows) on the
+// block-scaled FP8 matrix instruction.
+hipError_t launch_down1_q2k(const Down1Params& p, hipStream_t s);
 // Token-grouped Q2_K down (T > 1) on the bf16 matrix instruction: route-weighted
 // partials [pairs][rows] for the combine.
 bool dn_q2k_fits(int rows, int cols, long pairs);

@@ -92,10 +92,10 @@ def test_single_token_activation_outliers(fmt):
 
 @pytest.mark.parametrize("T", [1, 16])
 def test_q2k_down_on_oracle_h_is_tight(T):
-    """Q2_K down (single-token GEMV at T=1, GEMV partials at T=16) fed an fp32 h of
-    silu(g) * u values: the hi + lo bf16 split of h keeps 16 significant bits, and the
-    sub-block sums removed by the min term are taken from the same split values,
-    so the only rounding left is fp32 accumulation."""
+    """Q2_K down (the block-scaled kernel, one grid row per token at T=16) fed an
+    fp32 h of silu(g) * u values: four E4M3 terms keep about 16 significant bits
+    of h, and the min term takes the exact sub-block sums of h, so the error stays
+    far below the projection tolerance."""
     say("q2k down tight", T)
     spec = workloads.LayerSpec(4096, 2048, 256, 6, mq.FMT_NVFP4, mq.FMT_Q2_K, seed=5200 + T)
     layer = workloads.build_layer(mq, spec)
