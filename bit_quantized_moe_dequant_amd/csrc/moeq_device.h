@@ -157,8 +157,14 @@ struct WView {
   int rows, cols;
 };
 
+// The IQ2_XXS GEMV takes its sign words from the LDS table (1) or makes them in
+// registers (0); the token-grouped kernels always use the table.
+#ifndef MOEQ_IQ2_SIGN_LDS
+#define MOEQ_IQ2_SIGN_LDS 0
+#endif
 struct Iq2Lds {
   uint32_t grid[256 * 4];  // codebook entry i as four bf16 pairs (values 0..255: sign bits clear)
+  u32x4 sgn[128];          // the four bf16-pair sign words of 7-bit sign code c (iq2_sign_words)
 };
 
 template <int FMT> struct Dec;
@@ -416,10 +422,26 @@ template <> struct Dec<FMT_Q2_K> {
 // IQ2_XXS: chunk = two 32-weight sub-blocks (a0, a1) of a superblock, weights
 // 64c .. 64c + 63 of it; side = the superblock's fp16 d. The codebook (as bf16
 // pairs) and the 128 sign masks (bits 15 and 31 of four words) live in LDS.
+// The four bf16-pair sign masks of one IQ2_XXS group from its 7-bit sign code c:
+// the 8-bit mask m is c plus its parity bit (an even number of negatives); word k
+// carries m bit 2k at bit 15 and m bit 2k + 1 at bit 31. With Y = m << 15 | m << 30
+// as a 64-bit value (two copies that do not overlap), word k is bits [2k, 2k + 32)
+// of Y, masked to 0x80008000.
+__device__ __forceinline__ void iq2_sign_words(uint32_t c, uint32_t* w) {
+  const uint32_t m = c | ((uint32_t)(__builtin_popcount(c) & 1) << 7);
+  const uint32_t ylo = (m << 15) | (m << 30), yhi = m >> 2;
+#pragma unroll
+  for (int k = 0; k < 4; k++) w[k] = __builtin_amdgcn_alignbit(yhi, ylo, 2 * k) & 0x80008000u;
+}
 __device__ __forceinline__ void iq2_fill_lds(Iq2Lds* t, const uint8_t* grid, int tid, int nthreads) {
   for (int i = tid; i < 256 * 4; i += nthreads) {
     uint32_t g0 = grid[2 * i], g1 = grid[2 * i + 1];
     t->grid[i] = (f32_bf16_rne((float)g0)) | (f32_bf16_rne((float)g1) << 16);
+  }
+  for (int c = tid; c < 128; c += nthreads) {
+    uint32_t m[4];
+    iq2_sign_words((uint32_t)c, m);
+    t->sgn[c] = u32x4{m[0], m[1], m[2], m[3]};
   }
 }
 // The same table in two halves, for a 256-thread work-group that should not wait
@@ -438,19 +460,15 @@ __device__ __forceinline__ void iq2_store_entry(Iq2Lds* t, const Iq2Entry& e, in
 #pragma unroll
   for (int k = 0; k < 4; k++)
     t->grid[4 * tid + k] = f32_bf16_rne((float)e.b[2 * k]) | (f32_bf16_rne((float)e.b[2 * k + 1]) << 16);
+#if MOEQ_IQ2_SIGN_LDS
+  if (tid < 128) {
+    uint32_t m[4];
+    iq2_sign_words((uint32_t)tid, m);
+    t->sgn[tid] = u32x4{m[0], m[1], m[2], m[3]};
+  }
+#endif
 }
 
-// The four bf16-pair sign masks of one IQ2_XXS group from its 7-bit sign code c:
-// the 8-bit mask m is c plus its parity bit (an even number of negatives); word k
-// carries m bit 2k at bit 15 and m bit 2k + 1 at bit 31. With Y = m << 15 | m << 30
-// as a 64-bit value (two copies that do not overlap), word k is bits [2k, 2k + 32)
-// of Y, masked to 0x80008000.
-__device__ __forceinline__ void iq2_sign_words(uint32_t c, uint32_t* w) {
-  const uint32_t m = c | ((uint32_t)(__builtin_popcount(c) & 1) << 7);
-  const uint32_t ylo = (m << 15) | (m << 30), yhi = m >> 2;
-#pragma unroll
-  for (int k = 0; k < 4; k++) w[k] = __builtin_amdgcn_alignbit(yhi, ylo, 2 * k) & 0x80008000u;
-}
 template <> struct Dec<FMT_IQ2_XXS> {
   static constexpr int WPC = 64;
   typedef uint32_t Side;
@@ -484,8 +502,17 @@ template <> struct Dec<FMT_IQ2_XXS> {
         uint32_t gi = (a0 >> (8 * l)) & 0xFFu;
         uint32_t c = (a1 >> (7 * l)) & 0x7Fu;
         u32x4 g = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
+#if MOEQ_IQ2_SIGN_LDS
+        const u32x4 mv = t->sgn[c];
+        const uint32_t m[4] = {mv[0], mv[1], mv[2], mv[3]};
+#else
+        // In registers: the GEMV is bound by its codebook reads from LDS and the VALU
+        // together, and a second LDS read per group (the sign table) cost more than
+        // the ten VALU operations it saves (bs=1 IQ2_XXS + Q2_K layer 27.4 against
+        // 26.8 us).
         uint32_t m[4];
-        iq2_sign_words(c, m);  // in registers: an LDS lookup per group costs more here
+        iq2_sign_words(c, m);
+#endif
         // sign bits of the codebook words are clear, so OR applies the signs
 #pragma unroll
         for (int k = 0; k < 4; k++) S = dotp<ACT, 64>(g[k] | m[k], x, 16 * j + 4 * l + k, S);

@@ -453,11 +453,20 @@ constexpr int GEMV_UB = MOEQ_GEMV_UB, GEMV_NB = MOEQ_GEMV_NB, DOWN1_UB = MOEQ_DO
 // IQ2_XXS decodes at several times the ALU cost per byte of the other formats: its
 // four rows go in two batches of two, so the first batch's arithmetic overlaps
 // the second's transfer; the cheaper formats do better with one batch of four.
+#ifndef MOEQ_IQ2_UB
+#define MOEQ_IQ2_UB 2  // IQ2_XXS rows per batch
+#endif
+#ifndef MOEQ_IQ2_NB
+#define MOEQ_IQ2_NB 1  // IQ2_XXS row batches per wave
+#endif
 template <int FMT> struct GemvRows {
-  static constexpr int UB = FMT == FMT_IQ2_XXS ? 2 : GEMV_UB;
-  static constexpr int NB = FMT == FMT_IQ2_XXS ? 2 : GEMV_NB;
-  static_assert(UB * NB == GEMV_UB * GEMV_NB, "rows per wave must not depend on the format");
+  static constexpr int UB = FMT == FMT_IQ2_XXS ? MOEQ_IQ2_UB : GEMV_UB;
+  static constexpr int NB = FMT == FMT_IQ2_XXS ? MOEQ_IQ2_NB : GEMV_NB;
 };
+// Rows per wave of the GEMV for a format (the host sizes the grid with it).
+static int gemv_rows_per_wave(int fmt) {
+  return fmt == FMT_IQ2_XXS ? GemvRows<FMT_IQ2_XXS>::UB * GemvRows<FMT_IQ2_XXS>::NB : GEMV_UB * GEMV_NB;
+}
 
 // Token tile of the wide (several pairs per expert) launches. Every token of the
 // tile keeps its activation slices in registers for all of a lane's chunks, so the
@@ -512,7 +521,7 @@ hipError_t launch_gemv(int fmt, int epi, const GemvParams& p, int n_slots, int m
   q.lpr = lpr;
   q.chunks = p.cols / weights_per_chunk(fmt);
   int rw_rows = 64 / lpr;
-  q.U = GEMV_UB * GEMV_NB;
+  q.U = gemv_rows_per_wave(fmt);
   q.rows_per_wg = 4 * q.U * rw_rows;
   dim3 g((unsigned)((p.rows + q.rows_per_wg - 1) / q.rows_per_wg), (unsigned)n_slots);
   switch (fmt) {

@@ -77,14 +77,7 @@ __device__ __forceinline__ void gi_issue(const GiStreams& st, int sb, GiBuf& b) 
     b.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, st.x_off + 64 * j, sb * 512, 0));
 }
 
-// The four sign words of every 7-bit sign code (iq2_sign_words), looked up per
-// group: one LDS read in place of about a dozen VALU operations.
-struct GiSigns {
-  u32x4 w[128];
-};
-
-__device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* t, const GiSigns* sg,
-                                           f32x4_t (&acc)[2]) {
+__device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* t, f32x4_t (&acc)[2]) {
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const float d8 = half_bits_f32(b.d[mt]) * 0.125f;
@@ -95,7 +88,7 @@ __device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* 
       const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
       const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
       const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
-      const u32x4 m = sg->w[code];
+      const u32x4 m = t->sgn[code];
       // sign bits of the codebook words are clear, so OR applies the signs
       const u32x4 wv = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
       c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.x[j]),
@@ -114,13 +107,7 @@ __device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* 
 
 __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_gu_iq2(GemvParams P) {
   __shared__ Iq2Lds lds_tab[1];
-  __shared__ GiSigns signs[1];
   iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
-  if (threadIdx.x < 128) {
-    uint32_t m[4];
-    iq2_sign_words(threadIdx.x, m);
-    signs[0].w[threadIdx.x] = u32x4{m[0], m[1], m[2], m[3]};
-  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -168,11 +155,11 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
     for (int sb = 0;; sb += 2) {
       gi_issue(st, min(sb + 1, nsb - 1), B);
       __builtin_amdgcn_sched_barrier(0);
-      gi_compute(A, g, &lds_tab[0], &signs[0], acc);
+      gi_compute(A, g, &lds_tab[0], acc);
       if (sb + 1 >= nsb) break;
       gi_issue(st, min(sb + 2, nsb - 1), A);
       __builtin_amdgcn_sched_barrier(0);
-      gi_compute(B, g, &lds_tab[0], &signs[0], acc);
+      gi_compute(B, g, &lds_tab[0], acc);
       if (sb + 2 >= nsb) break;
     }
     // The final prefetch is never used: let it land before the registers are reused.
@@ -224,7 +211,7 @@ struct GwStage {
 // One superblock: each sub-block is decoded once (both matrices) and applied to
 // the pass's tiles, whose activations come from LDS.
 __device__ __forceinline__ void gw_compute(int nt, const GwBuf& b, const GwStage& xs, int n, int g, const Iq2Lds* t,
-                                           const GiSigns* sg, f32x4_t (&acc)[GW_NT][2]) {
+                                           f32x4_t (&acc)[GW_NT][2]) {
   float d8[2];
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) d8[mt] = half_bits_f32(b.d[mt]) * 0.125f;
@@ -238,7 +225,7 @@ __device__ __forceinline__ void gw_compute(int nt, const GwBuf& b, const GwStage
       const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
       const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
       const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
-      const u32x4 m = sg->w[code];
+      const u32x4 m = t->sgn[code];
       wv[mt] = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
       db[mt] = d8[mt] * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
     }
@@ -261,15 +248,9 @@ __device__ __forceinline__ void gw_compute(int nt, const GwBuf& b, const GwStage
 
 __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_gu_iq2_wide(GemvParams P) {
   __shared__ Iq2Lds lds_tab[1];
-  __shared__ GiSigns signs[1];
   __shared__ GwStage stg[2];
   __shared__ int s_pair[16 * GW_NT];
   iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
-  if (threadIdx.x < 128) {
-    uint32_t m[4];
-    iq2_sign_words(threadIdx.x, m);
-    signs[0].w[threadIdx.x] = u32x4{m[0], m[1], m[2], m[3]};
-  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -348,7 +329,7 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
             for (int i = 0; i < 4; i++) stg[k].x[sidx[u] + i] = v[k][u][i];
           xload(min(sb + k + 2, nsb - 1), v[k]);
           __syncthreads();
-          gw_compute(nt, W[k], stg[k], n, g, &lds_tab[0], &signs[0], acc);
+          gw_compute(nt, W[k], stg[k], n, g, &lds_tab[0], acc);
           gw_issue(st, min(sb + k + 2, nsb - 1), W[k]);
         }
       }
@@ -600,7 +581,7 @@ __device__ __forceinline__ void gd_stage_write(const u32x4 (&v)[4], int tm, int 
 }
 
 __device__ __forceinline__ void gd_compute(const GdW& b, const GdStage& s, int n, int g, const Iq2Lds* t,
-                                           const GiSigns* sg, f32x4_t& acc) {
+                                           f32x4_t& acc) {
   const float d8 = half_bits_f32(b.d) * 0.125f;
 #pragma unroll
   for (int j = 0; j < 8; j++) {
@@ -608,7 +589,7 @@ __device__ __forceinline__ void gd_compute(const GdW& b, const GdStage& s, int n
     const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
     const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
     const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
-    const u32x4 m = sg->w[code];
+    const u32x4 m = t->sgn[code];
     const u32x4 wv = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
     const int base = ((j * 16 + n) * 4 + g) * 2;  // A row n = token n
     f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, s.a[base]),
@@ -624,16 +605,10 @@ __device__ __forceinline__ void gd_compute(const GdW& b, const GdStage& s, int n
 
 __global__ __launch_bounds__(64 * GI_WAVES) void k_dn_iq2(GemvParams P) {
   __shared__ Iq2Lds lds_tab[1];
-  __shared__ GiSigns signs[1];
   __shared__ GdStage stg[2];
   __shared__ int s_pair[16];
   __shared__ float s_rw[16];
   iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
-  if (threadIdx.x < 128) {
-    uint32_t m[4];
-    iq2_sign_words(threadIdx.x, m);
-    signs[0].w[threadIdx.x] = u32x4{m[0], m[1], m[2], m[3]};
-  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -691,7 +666,7 @@ __global__ __launch_bounds__(64 * GI_WAVES) void k_dn_iq2(GemvParams P) {
           gd_stage_write(v[k], tm, tj >> 1, tj & 1, stg[k]);
           xload(min(sb + k + 2, nsb - 1), v[k]);
           __syncthreads();
-          gd_compute(W[k], stg[k], n, g, &lds_tab[0], &signs[0], acc);
+          gd_compute(W[k], stg[k], n, g, &lds_tab[0], acc);
           gd_wload(wr, sr, w_off, s_off, min(sb + k + 2, nsb - 1), W[k]);
         }
       }
