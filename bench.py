@@ -18,6 +18,8 @@ workload on this host).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --workload iq2_q2k_43 --tokens 2048   # a batched layer: us/layer only
+    python bench.py --workload iq2_q2k_43 --layers 43 [--tokens 64]   # 43 distinct layers per step
+    python bench.py --workload dense_linear --fmt mxfp8_tiled [--tokens 16]   # a dense FP8 linear
 """
 from __future__ import annotations
 
@@ -297,6 +299,97 @@ def run_prefill(args, wl):
     print(json.dumps(out), flush=True)
 
 
+FMT_LABEL = {1: "MXFP4 (e2m1 + e8m0/32)", 2: "NVFP4 (e2m1 + e4m3/16 + fp32 scale_2)", 3: "Q2_K", 4: "IQ2_XXS",
+             5: "FP8 E4M3 + UE8M0/128x128"}
+GU_KERNEL = {
+    1: "gate/up + SwiGLU: MXFP4 weights straight into v_mfma_scale_f32_16x16x128_f8f6f4 (bf16 token as two E4M3 terms)",
+    2: "gate/up + SwiGLU: NVFP4 weights into v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 scale per 16 on the results",
+    4: "gate/up + SwiGLU: IQ2_XXS dequant-GEMV (codebook in LDS, exact bf16 weights, v_dot2_f32_bf16)",
+}
+
+
+def run_layers(args, wl):
+    """Decode through N distinct layers back to back (--layers N, e.g. the 43 MoE
+    layers of the 2-bit hybrid model): N layers are built with their own weights
+    (43 x 1.8 GB for IQ2_XXS + Q2_K, far beyond the 256 MB MALL), and one step is one
+    forward of every layer at T tokens, each layer with its own activations and a
+    fresh uniform top-k per token. K steps are captured in one HIP graph and timed
+    with HIP events; it prints us per layer, us per step and tokens/s through the
+    stack. Not the headline metric."""
+    import torch
+
+    import bit_quantized_moe_dequant_amd as mq
+    from bit_quantized_moe_dequant_amd import synth, workloads
+
+    N, T, K, W = args.layers, args.tokens, args.steps, args.warmup
+    base = wl.spec
+    log(f"workload {wl.name}: building {N} layers ({base.n_experts} experts each) on the device")
+    layers = []
+    for li in range(N):
+        spec = workloads.LayerSpec(base.hidden, base.inter, base.n_experts, base.top_k, base.fmt_gate_up,
+                                   base.fmt_down, base.seed, li)
+        layers.append(workloads.build_layer(mq, spec))
+    torch.cuda.synchronize()
+    all_bytes = sum(l.expert_bytes() * l.n_experts for l in layers)
+    log(f"built: {all_bytes / 1e9:.1f} GB of weights")
+    xs = [torch.from_numpy(synth.activations_bf16(base.seed + 11 * li, T, base.hidden).view(np.int16)).cuda().view(
+        torch.bfloat16) for li in range(N)]
+    routes = [[synth.uniform_routing(base.seed + 1000 * li + 7 * i, T, base.n_experts, base.top_k)
+               for li in range(N)] for i in range(W + K)]
+    ids_t = [[torch.from_numpy(r[0]).cuda() for r in step] for step in routes]
+    rw_t = [[torch.from_numpy(r[1]).cuda() for r in step] for step in routes]
+    y = torch.empty((T, base.hidden), dtype=torch.float32, device="cuda")
+    ws = layers[0].workspace(T)
+    touched = float(np.mean([np.unique(r[0]).size for step in routes[W:] for r in step]))
+    step_bytes = N * touched * layers[0].expert_bytes()
+
+    def step(i):
+        for li in range(N):
+            mq.expert_forward(layers[li], xs[li], ids_t[i][li], rw_t[i][li], y=y, ws=ws)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(W + i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / K
+    err = mq.check_device_error(ws)
+    if err:
+        sys.exit(f"device error word {err:#x}")
+    log(f"{K} steps through {N} layers at T={T}: {ms_per_step * 1e3:.1f} us/step, "
+        f"{ms_per_step * 1e3 / N:.2f} us/layer")
+    print(json.dumps({
+        "metric": f"routed-MoE decode through {N} layers at T={T}: us/layer (not the headline)",
+        "value": round(ms_per_step * 1e3 / N, 3),
+        "unit": "us/layer",
+        "higher_is_better": False,
+        "steps": K,
+        "warmup": W,
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "experts_touched_per_layer": round(touched, 1),
+        "weight_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": N, "tokens_per_step": T,
+                   "weight_bytes_all_layers": all_bytes,
+                   "routing": "uniform top-k per token, fresh per step and layer",
+                   "launch": "HIP graph of the timed steps"},
+    }), flush=True)
+
+
 def run_batch(args, wl):
     """A decode workload at T > 1 tokens per step (--tokens): one step = one MoE layer
     over T tokens with a fresh uniform top-k per token (routing, gate/up, down,
@@ -427,6 +520,8 @@ def main():
                     help="decode workloads: tokens per step (T > 1 prints a separate us/layer line)")
     ap.add_argument("--fmt", default="mxfp8_tiled",
                     help="dense_linear workload: fp8_b128, fp8_b32, mxfp8 or mxfp8_tiled")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="decode through this many distinct layers per step (e.g. 43 for iq2_q2k_43)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -458,9 +553,11 @@ def main():
         return run_dense_linear(args)
     wl = workloads.WORKLOADS[args.workload]
     if args.steps is None:
-        args.steps = 100 if wl.prefill else (20 if args.tokens > 1 else 2000)
+        args.steps = 100 if wl.prefill else (20 if args.tokens > 1 or args.layers > 1 else 2000)
     if wl.prefill:
         return run_prefill(args, wl)
+    if args.layers > 1:
+        return run_layers(args, wl)
     if args.tokens > 1:
         return run_batch(args, wl)
     spec = wl.spec
@@ -553,8 +650,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name,
-            "description": "DeepSeek-V4-Flash-shaped routed-MoE layer, bs=1 decode: hidden 4096, "
-                           "256 experts, intermediate 2048, top-6, MXFP4 gate/up/down (e2m1 + e8m0/32)",
+            "description": f"DeepSeek-V4-Flash-shaped routed-MoE layer, bs=1 decode: hidden {spec.hidden}, "
+                           f"{spec.n_experts} experts, intermediate {spec.inter}, top-{spec.top_k}, "
+                           f"gate/up {FMT_LABEL[spec.fmt_gate_up]}, down {FMT_LABEL[spec.fmt_down]}",
             "tokens_per_step": 1,
             "weight_bytes_per_step": step_bytes,
             "routing": "uniform top-6 per step, no expert repeated within 42 steps (cold)",
@@ -565,7 +663,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "moe_tokens_per_s_43_layers": round(1e3 / (ms_per_step * 43), 1),
         "roofline": {
-            "kernel": "gate/up + SwiGLU: MXFP4 weights straight into v_mfma_scale_f32_16x16x128_f8f6f4 (bf16 token as two E4M3 terms)",
+            "kernel": GU_KERNEL.get(spec.fmt_gate_up, "gate/up + SwiGLU dequant-GEMV"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
