@@ -174,3 +174,36 @@ def test_mixed_iq2_gate_up_mxfp4_down_forward(T, sample):
     err = rel_err(y[toks], ref)
     say("err", err)
     assert err < TOL
+
+
+@pytest.mark.parametrize("T,E,K", [(48, 64, 6), (40, 2, 2), (130, 2, 2)])
+def test_iq2_grouped_down_tiles(T, E, K):
+    """The token-grouped IQ2_XXS down fed the oracle's own h: T = 48 over 64 experts
+    (4.5 pairs per touched expert: one partial 16-token tile each), T = 40 and 130
+    over two experts with top-2 (three and nine tiles per expert, the last partial).
+    One out-of-range id must add nothing."""
+    say("iq2 grouped down", T, E, K)
+    spec = workloads.LayerSpec(1024, 512, E, K, mq.FMT_MXFP4, mq.FMT_IQ2_XXS, seed=5500 + T)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, E, K)
+    x = synth.activations_bf16(spec.seed + 1, T, 1024)
+    rw0 = rw.copy()
+    rw0[1, 0] = 0.0  # the pair whose id goes out of range contributes nothing
+    wfn = oracle_weight_fn(spec)
+    toks = list(range(T)) if T <= 48 else [0, 1, 47, 48, 96, 129]
+    ref_y, ref_h = moe.moe_layer(x[toks], ids[toks], rw0[toks], wfn)
+    _, h_all = moe.moe_layer(x, ids, rw, wfn)
+    bad = ids.copy()
+    bad[1, 0] = 999
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    it = cuda(bad)
+    mq.route(layer, it, ws=ws)
+    h = torch.from_numpy(np.ascontiguousarray(h_all, dtype=np.float32)).cuda()
+    y = mq.down(layer, h, it, cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    err = rel_err(y[toks], ref_y)
+    say("err", err)
+    assert err < TOL
+    del layer
+    torch.cuda.empty_cache()
