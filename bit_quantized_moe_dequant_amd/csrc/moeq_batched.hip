@@ -15,10 +15,12 @@
 // A pair is a (token, slot) of the routing; the route table (the counting sort of
 // the pairs by expert) gives each work-group its expert and the expert's pairs.
 //
-// Work: a work-group is (routed expert, 16 weight rows), eight waves (gate/up) or
-// four (down) on contiguous runs of K steps; all weight loads of a wave go out after the first tile's
-// activations are converted, stay in registers and serve every tile of the
-// expert's pairs; the waves' partial sums meet in LDS and are added in wave order.
+// Work: a work-group is (routed expert, 16 weight rows), four waves on contiguous
+// runs of K steps; a wave issues the first tile's
+// activation loads, then all of its weight loads, then converts the activations
+// (waiting only for them); the weights stay in registers and serve every tile of
+// the expert's pairs; the waves' partial sums meet in LDS and are added in wave
+// order.
 // Gate/up writes h[pair][row] = silu(g) * u; down writes route-weighted partials
 // [pair][row] for the slot-order combine. The bucket of out-of-range ids writes
 // zeros.
@@ -37,11 +39,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int GB_WAVES = 4;         // down: four waves of up to eight K steps (K <= 2048 uses four)
 constexpr int GB_NT = 64 * GB_WAVES;
 constexpr int GB_STEPS = 8;
-// The first tile's activations are converted before the weight loads are issued
-// (1) or after (0).
-#ifndef MOEQ_G_XFIRST
-#define MOEQ_G_XFIRST 1
-#endif
 #ifndef MOEQ_GU_G_WAVES
 #define MOEQ_GU_G_WAVES 4
 #endif
@@ -91,11 +88,12 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
   const int rn = min(n0 + n, P.rows - 1);
   constexpr int XC = GU_TILE * GU_KMAX / 16 / GU_NT;  // chunk loads per thread per tile, at most
 
-  // A tile's tokens -> two E4M3 terms in LDS (every load first, then the conversion).
-  auto stage = [&](int m0) {
+  // A tile's tokens -> two E4M3 terms in LDS: stage_load issues the loads,
+  // stage_convert converts and stores (it waits only for those loads).
+  u32x4 xa[XC], xb[XC];
+  auto stage_load = [&](int m0) {
     const int tn = min(GU_TILE, M - m0);
     const int nc = (tn * cpt + GU_NT - 1) / GU_NT;  // uniform
-    u32x4 xa[XC], xb[XC];
 #pragma unroll
     for (int j = 0; j < XC; j++) {
       xa[j] = u32x4{0u, 0u, 0u, 0u};
@@ -108,6 +106,10 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
         xb[j] = ld16(xr + 8);
       }
     }
+  };
+  auto stage_convert = [&](int m0) {
+    const int tn = min(GU_TILE, M - m0);
+    const int nc = (tn * cpt + GU_NT - 1) / GU_NT;  // uniform
 #pragma unroll
     for (int j = 0; j < XC; j++) {
       if (j < nc) {
@@ -126,7 +128,9 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
     }
   };
 
-  if (MOEQ_G_XFIRST) stage(0);
+  // The first tile's activation loads, then every weight load of the wave, then the
+  // conversion (which waits only for the activations).
+  stage_load(0);
   __builtin_amdgcn_sched_barrier(0);
   u32x4 q[2][GU_STEPS];
   u32x4 sbv4[2][GU_STEPS / 4];
@@ -141,14 +145,15 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
       q[mt][i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (!MOEQ_G_XFIRST) stage(0);
+  stage_convert(0);
 
   const int pj = n >> 1, term = n & 1;  // this lane's A row: pair pj of the tile, its term
   for (int m0 = 0; m0 < M; m0 += GU_TILE) {
     const int tn = min(GU_TILE, M - m0);
     if (m0 > 0) {
       __syncthreads();  // the previous tile has read the staging and the partials
-      stage(m0);
+      stage_load(m0);
+      stage_convert(m0);
     }
     __syncthreads();
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -232,10 +237,10 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
   const int rn = min(n0 + n, P.rows - 1);
   constexpr int XC = (DN_TILE * DN_KMAX / 16 + GB_NT - 1) / GB_NT;
 
-  auto stage = [&](int m0) {
+  u32x4 hv[XC][4];
+  auto stage_load = [&](int m0) {
     const int tn = min(DN_TILE, M - m0);
     const int nc = (tn * cpt + GB_NT - 1) / GB_NT;  // uniform
-    u32x4 hv[XC][4];
 #pragma unroll
     for (int j = 0; j < XC; j++) {
 #pragma unroll
@@ -248,6 +253,10 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
         for (int i = 0; i < 4; i++) hv[j][i] = ld16(hr + 4 * i);
       }
     }
+  };
+  auto stage_convert = [&](int m0) {
+    const int tn = min(DN_TILE, M - m0);
+    const int nc = (tn * cpt + GB_NT - 1) / GB_NT;  // uniform
 #pragma unroll
     for (int j = 0; j < XC; j++) {
       if (j < nc) {
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
     }
   };
 
-  if (MOEQ_G_XFIRST) stage(0);
+  stage_load(0);
   __builtin_amdgcn_sched_barrier(0);
   u32x4 q[GB_STEPS];
   u32x4 sbv4[GB_STEPS / 4];
@@ -279,14 +288,15 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
     for (int i = 0; i < GB_STEPS; i++) q[i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (!MOEQ_G_XFIRST) stage(0);
+  stage_convert(0);
 
   const int pj = n / 3, term = n % 3;  // this lane's A row (row 15 unused)
   for (int m0 = 0; m0 < M; m0 += DN_TILE) {
     const int tn = min(DN_TILE, M - m0);
     if (m0 > 0) {
       __syncthreads();
-      stage(m0);
+      stage_load(m0);
+      stage_convert(m0);
     }
     __syncthreads();
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
