@@ -232,29 +232,40 @@ bool scales16(const moeq_weight& w) {
   return aligned(w.scales, 16) && (w.n_experts == 1 || w.scale_expert_stride % 16 == 0);
 }
 
-// An all-MXFP4 layer with at most this many tokens runs the single-token
-// matrix-unit kernels over every (token, slot) pair directly: no routing, no
-// partials and no combine (an expert routed by several tokens is read once per
-// token).
-#ifndef MOEQ_MX4_DIRECT_MAX_T
-#define MOEQ_MX4_DIRECT_MAX_T 32
+// Decode of a few tokens without grouping: the single-token kernels run over every
+// (token, slot) pair directly, with no routing, no partials and no combine (an
+// expert routed by several tokens is read once per pair). The gate/up takes this
+// path for MXFP4 up to MOEQ_FP4_DIRECT_MAX_T tokens and for NVFP4 up to
+// MOEQ_NV4_DIRECT_MAX_T (the block-scaled matrix-unit kernels; NVFP4 + Q2_K at
+// T = 2 / 8 / 16 / 32: 41.8 / 149 / 264 / 485 us against 49.1 / 160 / 270 / 477 us
+// grouped); the down for MXFP4 up to MOEQ_FP4_DIRECT_MAX_T, for Q2_K below a load
+// of MOEQ_Q2K_DIRECT_BELOW pairs per touched expert (0 turns that off). The routing
+// kernel runs only when a projection takes the grouped path.
+#ifndef MOEQ_FP4_DIRECT_MAX_T
+#define MOEQ_FP4_DIRECT_MAX_T 32
 #endif
-bool mx4_direct(const moeq_layer* L, int T) {
-  return T >= 1 && T <= MOEQ_MX4_DIRECT_MAX_T && L->gate.fmt == MOEQ_FMT_MXFP4 && L->up.fmt == MOEQ_FMT_MXFP4 &&
-         L->down.fmt == MOEQ_FMT_MXFP4 && gu1_mx4_fits(L->inter, L->hidden) &&
-         down1_mx4_fits(L->hidden, L->inter, L->top_k) && scales16(L->gate) && scales16(L->up) && scales16(L->down);
-}
-
-// A Q2_K down with fewer pairs per touched expert than this runs the single-token
-// block-scaled kernel once per token (a grid row each): every routed expert is read
-// once per (token, slot) pair instead of once, but with no partials, no combine and
-// the matrix instruction instead of the grouped GEMV (0 turns the path off).
+#ifndef MOEQ_NV4_DIRECT_MAX_T
+#define MOEQ_NV4_DIRECT_MAX_T 16
+#endif
 #ifndef MOEQ_Q2K_DIRECT_BELOW
 #define MOEQ_Q2K_DIRECT_BELOW 2.5
 #endif
-bool q2k_direct(const moeq_layer* L, int T, const float* h) {
-  return T >= 1 && L->down.fmt == MOEQ_FMT_Q2_K && pairs_per_expert(L, T) < MOEQ_Q2K_DIRECT_BELOW &&
-         down1_q2k_fits(L->hidden, L->inter, L->top_k) && aligned(h, 16);
+bool gu_direct(const moeq_layer* L, int T) {
+  if (T == 1) return true;
+  const int max_t = L->gate.fmt == MOEQ_FMT_MXFP4 ? MOEQ_FP4_DIRECT_MAX_T
+                    : L->gate.fmt == MOEQ_FMT_NVFP4 ? MOEQ_NV4_DIRECT_MAX_T
+                                                    : 0;
+  return T >= 1 && T <= max_t && L->gate.fmt == L->up.fmt && gu1_mx4_fits(L->inter, L->hidden) &&
+         scales16(L->gate) && scales16(L->up);
+}
+bool dn_direct(const moeq_layer* L, int T, const float* h) {
+  if (T == 1) return true;
+  if (T < 1 || !aligned(h, 16)) return false;
+  if (L->down.fmt == MOEQ_FMT_MXFP4)
+    return T <= MOEQ_FP4_DIRECT_MAX_T && down1_mx4_fits(L->hidden, L->inter, L->top_k) && scales16(L->down);
+  if (L->down.fmt == MOEQ_FMT_Q2_K)
+    return pairs_per_expert(L, T) < MOEQ_Q2K_DIRECT_BELOW && down1_q2k_fits(L->hidden, L->inter, L->top_k);
+  return false;
 }
 
 int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, float* h, void* ws, const WsLayout& lay,
@@ -264,7 +275,7 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
   p.ids = ids;
   p.T = T;
   p.out = h;
-  if (T == 1 || mx4_direct(L, T)) {
+  if (gu_direct(L, T)) {
     p.mode = MODE_DIRECT;
     return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, T * L->top_k, 1, s, ev));
   }
@@ -281,7 +292,7 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
 
 int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const float* rw, int T, float* y, void* ws,
              const WsLayout& lay, hipStream_t s) {
-  if (T == 1 || mx4_direct(L, T) || q2k_direct(L, T, h)) {
+  if (dn_direct(L, T, h)) {
     Down1Params d;
     memset(&d, 0, sizeof(d));
     d.T = T;
@@ -632,7 +643,7 @@ int forward(const moeq_layer* L, const void* x, const int32_t* ids, const float*
             const WsLayout& lay, hipStream_t s) {
   int rc;
   float* h = (float*)((uint8_t*)ws + lay.h);
-  if (T > 1 && !mx4_direct(L, T)) {
+  if (T > 1 && !(gu_direct(L, T) && dn_direct(L, T, h))) {
     rc = hip_rc(launch_route(ids, T * L->top_k, L->n_experts, route_view(L, ws, lay), err_of(ws, lay), s));
     if (rc) return rc;
   }
