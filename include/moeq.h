@@ -9,12 +9,16 @@
  *   for token t routed to experts e_k with route weights w_k (k < top_k):
  *     h_k = silu(G_e x_t) * (U_e x_t),   y_t = sum_k w_k * (D_e h_k)
  *
- * At decode (few tokens) each projection streams the routed experts' weights
- * once: MXFP4 and NVFP4 single-token gate/up (and MXFP4 down) feed the FP4 codes
- * straight into the block-scaled matrix instruction, the other formats and shapes
- * decode on the VALU (dequantize + GEMV). When many tokens share an expert,
- * IQ2_XXS gate/up and Q2_K down decode once per 16-token tile for the bf16
- * matrix instructions. At prefill with MXFP4 weights it is a token-grouped GEMM
+ * At decode (few tokens) each projection streams the routed experts' weights:
+ * MXFP4 and NVFP4 gate/up and MXFP4 down feed the FP4 codes straight into the
+ * block-scaled matrix instruction, and the Q2_K down its 2-bit codes as FP8
+ * operands of the same instruction; IQ2_XXS and the remaining shapes decode on the
+ * VALU (dequantize + GEMV). Up to 32 tokens (16 for NVFP4 gate/up; Q2_K down below
+ * 2.5 pairs per touched expert) these kernels run over every (token, slot) pair
+ * with no routing step; beyond, each routed expert is read once per step for all
+ * of its tokens (MXFP4 on the block-scaled instruction; IQ2_XXS gate/up and Q2_K
+ * or IQ2_XXS down decoding once per 16-token tile for the bf16 matrix
+ * instructions). At prefill with MXFP4 weights it is a token-grouped GEMM
  * on the block-scaled FP4 matrix instructions, with activations quantised to
  * MXFP8 (fp4 weights times E4M3 activations: DeepSeekv4 Flash for 1x Spark forum
  * thread, second post). The decode paths agree with the exact layer to the
