@@ -247,11 +247,21 @@ bool scales16(const moeq_weight& w) {
 #ifndef MOEQ_NV4_DIRECT_MAX_T
 #define MOEQ_NV4_DIRECT_MAX_T 16
 #endif
+// IQ2_XXS gate/up: the dequantize + GEMV over every pair below this load (pairs per
+// touched expert): IQ2_XXS + Q2_K at T = 2 / 8 / 16 / 32 (1.0 / 1.1 / 1.2 / 1.4
+// pairs): 48.2 / 165 / 296 / 555 us against 72.3 / 198 / 344 / 564 us with the
+// token-grouped kernel, whose 16-token tiles are mostly empty there; at T = 48
+// (1.7 pairs) 799 against 758 us.
+#ifndef MOEQ_IQ2_DIRECT_BELOW
+#define MOEQ_IQ2_DIRECT_BELOW 1.5
+#endif
 #ifndef MOEQ_Q2K_DIRECT_BELOW
 #define MOEQ_Q2K_DIRECT_BELOW 2.5
 #endif
 bool gu_direct(const moeq_layer* L, int T) {
   if (T == 1) return true;
+  if (L->gate.fmt == MOEQ_FMT_IQ2_XXS)  // the dequantize + GEMV over every pair
+    return T >= 1 && L->up.fmt == MOEQ_FMT_IQ2_XXS && pairs_per_expert(L, T) < MOEQ_IQ2_DIRECT_BELOW;
   const int max_t = L->gate.fmt == MOEQ_FMT_MXFP4 ? MOEQ_FP4_DIRECT_MAX_T
                     : L->gate.fmt == MOEQ_FMT_NVFP4 ? MOEQ_NV4_DIRECT_MAX_T
                                                     : 0;

@@ -207,3 +207,33 @@ def test_iq2_grouped_down_tiles(T, E, K):
     assert err < TOL
     del layer
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [3, 8])
+def test_iq2_direct_few_tokens(T):
+    """IQ2_XXS gate/up + Q2_K down for a few tokens over 64 experts (about 1.1 and
+    1.4 pairs per touched expert): both projections run over every (token, slot)
+    pair without routing. One out-of-range id must give zero h and add nothing."""
+    say("iq2 direct", T)
+    spec = workloads.LayerSpec(1024, 512, 64, 6, mq.FMT_IQ2_XXS, mq.FMT_Q2_K, seed=5600 + T)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, 64, 6)
+    x = synth.activations_bf16(spec.seed + 1, T, 1024)
+    bad = ids.copy()
+    bad[T - 1, 4] = -3
+    rw0 = rw.copy()
+    rw0[T - 1, 4] = 0.0
+    wfn = oracle_weight_fn(spec)
+    ref_y, ref_h = moe.moe_layer(x, ids, rw0, wfn)
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    xt, it = x_tensor(x), cuda(bad)
+    y = mq.expert_forward(layer, xt, it, cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    h = mq.gate_up(layer, xt, it, ws=ws).cpu().numpy().reshape(T, 6, 512)
+    assert np.all(h[T - 1, 4] == 0.0)
+    ok = np.ones((T, 6), bool)
+    ok[T - 1, 4] = False
+    eh, ey = rel_err(h[ok], ref_h[ok]), rel_err(y, ref_y)
+    say("h err", eh, "y err", ey)
+    assert eh < TOL and ey < TOL

@@ -408,6 +408,7 @@ def test_single_expert_workload():
 
 @pytest.mark.parametrize("name,T,sample", [("mxfp4_layer", 1, None), ("nvfp4_q2k", 1, None),
                                             ("nvfp4_q2k", 16, [0, 7, 15]), ("iq2_q2k_43", 1, None),
+                                            ("iq2_q2k_43", 16, [0, 8, 15]),
                                             ("iq2_q2k_43", 64, [0, 31, 63])])
 def test_full_size_layer(name, T, sample):
     """Full-size layer (device-filled), the launch configuration the benchmark
