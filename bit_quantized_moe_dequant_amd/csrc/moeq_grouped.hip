@@ -589,7 +589,10 @@ __device__ __forceinline__ void gd_compute(const GdW& b, const GdStage& s, int n
     const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
     const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
     const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
-    const u32x4 m = t->sgn[code];
+    // sign words in registers here (mixed-layer prefill at T = 2048: 2360 against
+    // 2492 us with the LDS table, which the gate/up kernels keep)
+    uint32_t m[4];
+    iq2_sign_words(code, m);
     const u32x4 wv = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
     const int base = ((j * 16 + n) * 4 + g) * 2;  // A row n = token n
     f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, s.a[base]),
