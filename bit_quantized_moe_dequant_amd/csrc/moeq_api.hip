@@ -120,7 +120,7 @@ bool prefill_buffers(const moeq_layer* L, int T) {
 }
 
 struct WsLayout {
-  size_t route, h, partial, xq, xs, hq, hs, total;
+  size_t route, h, partial, xq, xs, hq, hs, dq, ds, total;
   int P;
   uint32_t* err;  // device error word the kernels OR into (null: the workspace's own)
 };
@@ -136,8 +136,15 @@ WsLayout ws_layout(const moeq_layer* L, int T) {
   off += align_up(P * L->inter * 4, 256);
   w.partial = off;
   off += T > 1 ? align_up(P * L->hidden * 4, 256) : 0;
-  w.xq = w.xs = w.hq = w.hs = 0;
+  w.xq = w.xs = w.hq = w.hs = w.dq = w.ds = 0;
   w.err = nullptr;
+  if (T > 1 && L->down.fmt == MOEQ_FMT_Q2_K && dn_q2k_g_fits(L->hidden, L->inter)) {
+    // digit planes of h for the grouped Q2_K down
+    w.dq = off;
+    off += align_up(dn_q2k_g_digit_bytes((long)P, L->inter), 256);
+    w.ds = off;
+    off += align_up(dn_q2k_g_scale_bytes((long)P, L->inter), 256);
+  }
   if (prefill_buffers(L, T)) {
     w.xq = off;
     off += align_up((size_t)T * L->hidden, 256);
@@ -211,15 +218,18 @@ bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >=
 #define MOEQ_IQ2_WIDE_FROM 8.0
 #endif
 
-// Q2_K down partials on the matrix instruction (decode once per 16 tokens) from
-// this many expected pairs per touched expert; below it most of a 16-token tile is
-// padding and the GEMV is faster (measured at 1.2 and 1.9 pairs: 415 vs 328 us and
-// 1199 vs 1159 us per layer). Above it the grouped kernel wins: at 3 and 6 pairs
-// (T = 128, 256 over 256 experts) the NVFP4 + Q2_K layer took 1415 and 1926 us
-// against 1845 and 3026 us with the GEMV; at 48 pairs the down took 4.5 ms against
-// 11.3 ms.
+// Q2_K down at T > 1 off the direct path: partials on the block-scaled FP8
+// instruction (each expert's weights read once, h's digits made once per pair)
+// below MOEQ_Q2K_G_BELOW pairs per touched expert, else on the bf16 instruction
+// (decode once per 16 tokens) from MOEQ_DN_Q2K_FROM pairs. The FP8 kernel was
+// faster at every load measured: IQ2_XXS + Q2_K layers at T = 64 / 256 / 2048 (2,
+// 6 and 48 pairs) took 782 / 1201 / 3448 us against 1108 (direct) / 1423 / 3768 us
+// (bf16). The bf16 kernel stays for h that is not 16-byte aligned.
 #ifndef MOEQ_DN_Q2K_FROM
 #define MOEQ_DN_Q2K_FROM 2.5
+#endif
+#ifndef MOEQ_Q2K_G_BELOW
+#define MOEQ_Q2K_G_BELOW 1e30
 #endif
 
 // MXFP4 decode at T > 1 on the block-scaled matrix instruction (1), or as GEMVs (0).
@@ -239,8 +249,10 @@ bool scales16(const moeq_weight& w) {
 // MOEQ_NV4_DIRECT_MAX_T (the block-scaled matrix-unit kernels; NVFP4 + Q2_K at
 // T = 2 / 8 / 16 / 32: 41.8 / 149 / 264 / 485 us against 49.1 / 160 / 270 / 477 us
 // grouped); the down for MXFP4 up to MOEQ_FP4_DIRECT_MAX_T, for Q2_K below a load
-// of MOEQ_Q2K_DIRECT_BELOW pairs per touched expert (0 turns that off). The routing
-// kernel runs only when a projection takes the grouped path.
+// of MOEQ_Q2K_DIRECT_BELOW pairs per touched expert (0 turns that off; NVFP4 + Q2_K
+// at T = 2 / 4 / 8 / 16 / 64: 46.3 / 87.3 / 160.0 / 294.6 / 1024 us direct against
+// 58.4 / 89.3 / 149.8 / 255.3 / 702 us with the grouped FP8 down). The routing kernel
+// runs only when a projection takes the grouped path.
 #ifndef MOEQ_FP4_DIRECT_MAX_T
 #define MOEQ_FP4_DIRECT_MAX_T 32
 #endif
@@ -256,7 +268,7 @@ bool scales16(const moeq_weight& w) {
 #define MOEQ_IQ2_DIRECT_BELOW 1.5
 #endif
 #ifndef MOEQ_Q2K_DIRECT_BELOW
-#define MOEQ_Q2K_DIRECT_BELOW 2.5
+#define MOEQ_Q2K_DIRECT_BELOW 1.06
 #endif
 bool gu_direct(const moeq_layer* L, int T) {
   if (T == 1) return true;
@@ -330,8 +342,11 @@ int run_down(const moeq_layer* L, const float* h, const int32_t* ids, const floa
   int slots = L->n_experts + 1;
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
   int rc;
-  if (L->down.fmt == MOEQ_FMT_Q2_K && pairs_per_expert(L, T) >= MOEQ_DN_Q2K_FROM &&
-      dn_q2k_fits(L->hidden, L->inter, (long)T * L->top_k))
+  const double ppe = pairs_per_expert(L, T);
+  if (L->down.fmt == MOEQ_FMT_Q2_K && ppe < MOEQ_Q2K_G_BELOW && lay.dq && aligned(h, 16))
+    rc = hip_rc(launch_dn_q2k_g(p, slots, (uint8_t*)ws + lay.dq, (uint8_t*)ws + lay.ds, s));
+  else if (L->down.fmt == MOEQ_FMT_Q2_K && ppe >= MOEQ_DN_Q2K_FROM &&
+           dn_q2k_fits(L->hidden, L->inter, (long)T * L->top_k))
     rc = hip_rc(launch_dn_q2k(p, slots, s));
   else if (L->down.fmt == MOEQ_FMT_IQ2_XXS && pairs_per_expert(L, T) >= MOEQ_DN_Q2K_FROM &&
            dn_q2k_fits(L->hidden, L->inter, (long)T * L->top_k))

@@ -56,40 +56,41 @@ constexpr int QD_SLOTS = 6;                         // routed slots (top-6)
 constexpr int QD_REC = 5;                           // dwords of a scale record
 constexpr int QD_WREC = 16 * QD_SB * QD_REC;        // a wave's records: 320 dwords
 
-// Four base-16 digits of 16 consecutive fp32 values (a Q2_K sub-block; v: 4 loads
-// of 4 values) on a grid of their own. With M their largest magnitude and s the
-// exponent with M / 2^s in [16, 32), digit t is an integer on the grid 2^(s - 4t):
-// d_0 = rint(v / 2^s) if that is at most 16, else twice rint(v / 2^(s+1)) (E4M3
-// holds every integer up to 16 but only even ones up to 32); then d_t =
-// rint(r_t / 2^(s - 4t)) with r_(t+1) = r_t - d_t 2^(s - 4t) (exact in fp32). So
-// |d_0| <= 32, |d_1| <= 16, |d_2|, |d_3| <= 8, every digit is an exact E4M3 value, and
-// |v - sum_t d_t 2^(s - 4t)| <= 2^(s - 13) <= 2^-17 M. store(t, j, code) gets the E4M3
-// codes of digit t of values 4j .. 4j + 3, scale(t, E) its e8m0 code E = s - 4t + 127
-// (clamped at 0, where the grid only gets coarser for tiny M).
-template <class Store, class Scale>
-__device__ __forceinline__ void h_digits(const u32x4 (&v)[4], Store&& store, Scale&& scale) {
-  float x[16];
+// Four digits of 4 NQ consecutive fp32 values (a Q2_K sub-block for NQ = 4, two for
+// NQ = 8; v: NQ loads of 4 values) on a grid of their own, in base 2^STEP. With M
+// their largest magnitude and s the exponent with M / 2^s in [16, 32), digit t is an
+// integer on the grid 2^(s - STEP t): d_t = rint(r_t / 2^(s - STEP t)) if that is at
+// most 16 in magnitude, else twice rint(r_t / 2^(s - STEP t + 1)) (E4M3 holds every
+// integer up to 16 but only even ones up to 32), with r_0 = v and r_(t+1) = r_t -
+// d_t 2^(s - STEP t) (exact in fp32). |r_0| < 2^(s + 5) and each later |r_t| is at
+// most one grid step of the digit before, so every |d_t| <= 32 is an exact E4M3
+// value (for STEP = 4 the later digits stay within 16 and skip the even case), and
+// |v - sum_t d_t 2^(s - STEP t)| <= 2^(s - 4 STEP + 3): 2^-17 M for STEP = 4 and
+// 2^-19 M for STEP = 5. store(t, j, code) gets the E4M3 codes of digit t of values
+// 4j .. 4j + 3, scale(t, E) its e8m0 code E = s - STEP t + 127 (clamped at 0, where
+// the grid only gets coarser for tiny M). (h_digits_of: the same for values that are
+// part of a larger block, whose largest magnitude is amax.)
+template <int NQ, int STEP, class Store, class Scale>
+__device__ __forceinline__ void h_digits_of(const u32x4 (&v)[NQ], float amax, Store&& store, Scale&& scale) {
+  float x[4 * NQ];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < NQ; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) x[4 * i + j] = u2f(v[i][j]);
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
   const int s = (int)((f2u(amax) >> 23) & 0xFFu) - 131;  // floor(log2 M) - 4 (zero or subnormal M: -131)
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    const int st = max(s - 4 * t, -127);
+    const int st = max(s - STEP * t, -127);
     const float inv = u2f((uint32_t)(127 - st) << 23);  // 2^-st
     const float sc = e8m0_f32((uint32_t)(st + 127));     // 2^st
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < NQ; j++) {
       float d[4];
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const float q = x[4 * j + k] * inv;
         d[k] = __builtin_rintf(q);
-        if (t == 0) d[k] = __builtin_fabsf(q) <= 16.f ? d[k] : 2.f * __builtin_rintf(0.5f * q);
+        if (t == 0 || STEP > 4) d[k] = __builtin_fabsf(q) <= 16.f ? d[k] : 2.f * __builtin_rintf(0.5f * q);
         x[4 * j + k] = __builtin_fmaf(-d[k], sc, x[4 * j + k]);
       }
       const i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, d[0], d[1], 1.0f, false);
@@ -98,6 +99,16 @@ __device__ __forceinline__ void h_digits(const u32x4 (&v)[4], Store&& store, Sca
     }
     scale(t, (uint32_t)(st + 127));
   }
+}
+
+template <int NQ, int STEP, class Store, class Scale>
+__device__ __forceinline__ void h_digits(const u32x4 (&v)[NQ], Store&& store, Scale&& scale) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NQ; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(u2f(v[i][j])));
+  h_digits_of<NQ, STEP>(v, amax, store, scale);
 }
 
 struct QdStage {
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(64 * QD_KPARTS * QD_SLOTS) QD_ATTR void k_down1_q2k
 
   // h -> four digits and the exact sum of each 16-value sub-block.
   if (16 * (int)threadIdx.x < total) {
-    h_digits(
+    h_digits<4, 4>(
         hv, [&](int t, int j, uint32_t w) { *reinterpret_cast<uint32_t*>(&st.code[t][v0i + 4 * j]) = w; },
         [&](int t, uint32_t E) { st.sc[t][v0i / 16] = (uint8_t)E; });
     float s = 0.f;
@@ -254,6 +265,256 @@ __global__ __launch_bounds__(64 * QD_KPARTS * QD_SLOTS) QD_ATTR void k_down1_q2k
   if (!ok && blockIdx.x == 0 && lane == 0 && part == 0) atomicOr(P.err, 1u);
 }
 
+
+// ---------------------------------------------------------------- token-grouped (T > 1)
+// The down projection of a batch, each routed expert's weights read once for all of
+// its pairs, on the same instruction. The weights stay operand B (16 columns = 16
+// weight rows; lane (row n, group g) holds chunk g of the row's superblock, planes
+// 2 pp and 2 pp + 1 as its two 16-byte halves in pass pp). Q2_K's sub-block scale
+// and min are folded into B: with sc = sl + 4 sh (sl, sh < 4) the products sl q and
+// sh q (at most 9) and the min m (at most 15) are integers below 16, and E4M3 codes
+// 0 .. 15 are exactly the values c 2^-9 (the subnormals and the first binade share
+// one spacing), so a byte-wise multiply of the crumbs makes each operand and the B
+// scales 2^9, 2^11 and 2^9 make them sl q, 4 sh q and m. A whole 128-wide K step then
+// accumulates in one instruction: for a row, sum over K of (sl + 4 sh) q h = sc sum q h
+// per sub-block, and sum of m h = m times the sub-block's sum of h; only d and dmin
+// remain, once per superblock.
+//
+// Operand A: four pairs by four digits (row 4 i + t: digit t of pair i) of h, now on
+// the grid of each 32-value block, since every row spans the four scale blocks of
+// the step; a block's two sub-blocks sit in one scale block of the instruction (the
+// halves of lane groups 0, 1 or 2, 3). The digits are base 32 here (base 16 on the
+// wider grid kept too few bits: 1.0e-4 elementwise against the oracle). Digits and
+// products stay integers (at most 32 times 15 units), so each dot is exact and h
+// keeps 19 bits relative to its block's maximum. Output lane (n, g) register t is digit t of pair g against row n.
+//
+// k_q2k_digits writes every pair's digits once per step, in the operand order: per
+// (pair, superblock) 1024 code bytes [pp][half][group][digit][16] and 32 scale bytes
+// [pp][digit][scale group]. A work-group (one expert, 64 weight rows in four waves)
+// loads its weights and scale records for all of K into registers, then copies the
+// digits of up to 4 NG of the expert's pairs into LDS (one 16-byte piece per lane,
+// straight from memory into the operand order) and runs the pass; an expert with
+// more pairs takes further passes over the same weight registers. Outputs are
+// route-weighted partials per (pair, row) for the combine. One group per pass (NG =
+// 1: 34 KB of LDS, three work-groups per CU) ran faster than two (67.5 KB, two per
+// CU) at every batch measured, from 2 to 48 pairs per expert.
+constexpr int QG_WAVES = 4;
+constexpr int QG_ROWS = 16 * QG_WAVES;
+constexpr int QG_SB = 8;  // superblocks along K (K <= 2048)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// Bytes of x (each below 4) times f (below 4), byte by byte: one 16-bit pair multiply.
+__device__ __forceinline__ uint32_t crumb_mul(uint32_t x, uint32_t f) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, x) * __builtin_bit_cast(u16x2_t, f * 0x10001u));
+}
+
+// Four lanes per 32-value block of h (8 values each; the block's largest magnitude
+// by two lane exchanges): its four digits and their e8m0 codes.
+__global__ __launch_bounds__(256) void k_q2k_digits(const float* __restrict__ h, int nval8, int nsb,
+                                                    uint8_t* __restrict__ dq, uint8_t* __restrict__ dsc) {
+  const int i8 = blockIdx.x * 256 + (int)threadIdx.x;  // 8-value piece; nval8 is a multiple of 4
+  if (i8 >= nval8) return;                              // whole groups of four leave together
+  const int b = i8 >> 2, q = i8 & 3;
+  const int pair = b / (8 * nsb), r = b % (8 * nsb), sb = r >> 3, kb = r & 7;
+  const float* src = h + (size_t)i8 * 8;  // [pair][K]: piece i8 starts at value 8 i8
+  const u32x4 v[2] = {ld16(src), ld16(src + 4)};
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(u2f(v[i][j])));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 4));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, 4));
+  // Sub-blocks 2 kb, 2 kb + 1 of the superblock: pass pp, half, lane groups g0, g0 + 1
+  // (values 0-15 and 16-31 of the block, piece q in sub-block q >> 1 at byte 8 (q & 1));
+  // the scale of the pair's 32-wide block comes from lane group gs.
+  const int pp = (kb >> 1) & 1, half = kb & 1, g0 = 2 * (kb >> 2), gs = 2 * (kb & 1) + (kb >> 2);
+  uint8_t* cb = dq + ((size_t)pair * nsb + sb) * 1024 + (pp * 2 + half) * 256 + (g0 + (q >> 1)) * 64 + 8 * (q & 1);
+  uint8_t* sbp = dsc + ((size_t)pair * nsb + sb) * 32 + pp * 16 + gs;
+  uint32_t w[4][2];
+  h_digits_of<2, 5>(
+      v, amax, [&](int t, int j, uint32_t code) { w[t][j] = code; },
+      [&](int t, uint32_t E) {
+        if (q == 0) sbp[4 * t] = (uint8_t)E;
+      });
+#pragma unroll
+  for (int t = 0; t < 4; t++) *reinterpret_cast<u32x2*>(cb + 16 * t) = u32x2{w[t][0], w[t][1]};
+}
+
+// The instruction with A's scale taken from byte sel of sa (sel a constant once the
+// callers' loops are unrolled).
+__device__ __forceinline__ f32x4_t mfma_sel(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c, int sel, int sa,
+                                            int sbv) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sbv);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 1, sa, 0, sbv);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 2, sa, 0, sbv);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 3, sa, 0, sbv);
+  }
+}
+
+template <int NG>
+struct QgStage {
+  u32x4 code[QG_SB][NG][2][2][64];  // [sb][group][pp][half][lane]: lane 16 g + 4 i + t's A bytes
+  uint32_t sc[QG_SB][64];           // [sb][lane]: byte 2 G + pp = the lane's e8m0 for group G, pass pp
+};
+
+template <int NG>
+__global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const uint8_t* __restrict__ dq,
+                                                            const uint8_t* __restrict__ dsc) {
+  constexpr int CH = 4 * NG;  // pairs per pass
+  __shared__ QgStage<NG> st;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int slot = blockIdx.y;
+  if (slot >= P.route.n_slots()[0]) return;
+  const int e = P.route.slots()[slot];
+  const int pstart = P.route.offsets()[e];
+  const int M = P.route.offsets()[e + 1] - pstart;
+  const int r0 = blockIdx.x * QG_ROWS;
+  if (r0 >= P.rows || M <= 0) return;  // uniform per work-group: the barriers below are reached by all
+  const int32_t* perm = P.route.perm() + pstart;
+
+  if (e < 0 || e >= P.n_experts) {
+    // Out-of-range expert id (its bucket): its pairs contribute nothing.
+    for (int m = 0; m < M; m++)
+      for (int i = threadIdx.x; i < QG_ROWS; i += 64 * QG_WAVES)
+        if (r0 + i < P.rows) P.out[(size_t)perm[m] * P.rows + r0 + i] = 0.f;
+    return;
+  }
+
+  const int nsb = P.cols / 256;
+  const int n0 = r0 + 16 * wave;
+  const int rn = min(n0 + n, P.rows - 1);
+  // All of K for row rn: chunk g of each superblock, and the scale record dwords of
+  // chunk g's sub-blocks (planes 0, 1: dword 2 (g >> 1); planes 2, 3: the next) and
+  // d | dmin (superblocks past the end re-read the last and are not used).
+  const uint8_t* wrow = P.w[0].data + (size_t)e * P.w[0].estride + (size_t)rn * nsb * 64 + 16 * g;
+  const uint32_t* srow =
+      reinterpret_cast<const uint32_t*>(P.w[0].scales + (size_t)e * P.w[0].sestride + (size_t)rn * nsb * 20);
+  u32x4 q[QG_SB];
+  uint32_t rlo[QG_SB], rhi[QG_SB], rdd[QG_SB];
+#pragma unroll
+  for (int i = 0; i < QG_SB; i++) {
+    const int sbc = min(i, nsb - 1);
+    q[i] = ld16(wrow + sbc * 64);
+    rlo[i] = srow[5 * sbc + 2 * (g >> 1)];
+    rhi[i] = srow[5 * sbc + 2 * (g >> 1) + 1];
+    rdd[i] = srow[5 * sbc + 4];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int t = lane & 3, ip = (lane >> 2) & 3;  // this lane's A row: digit t of pair 4 G + ip
+  for (int c0 = 0; c0 < M; c0 += CH) {
+    if (c0 > 0) __syncthreads();  // the previous pass has read the stage
+    int pa[NG], po[NG];
+    float rwo[NG];
+#pragma unroll
+    for (int G = 0; G < NG; G++) {
+      pa[G] = perm[min(c0 + 4 * G + ip, M - 1)];  // pairs past the last repeat it and are not stored
+      po[G] = perm[min(c0 + 4 * G + g, M - 1)];
+      rwo[G] = P.rw[po[G]];
+    }
+    // Digit codes: wave w copies the (pass w >> 1, half w & 1) pieces of every
+    // superblock and group, lane l = 16 g + 4 ip + t taking (pair 4 G + ip, group g,
+    // digit t).
+    {
+      const int pp = wave >> 1, half = wave & 1;
+#pragma unroll
+      for (int i = 0; i < QG_SB; i++)
+#pragma unroll
+        for (int G = 0; G < NG; G++)
+          if (i < nsb) {
+            const uint8_t* src = dq + ((size_t)pa[G] * nsb + i) * 1024 + (pp * 2 + half) * 256 + g * 64 + t * 16;
+            __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)&st.code[i][G][pp][half][0], 16, 0, 0);
+          }
+    }
+    // Scale codes: thread (pair pl, superblock sx, piece pc) moves 8 bytes [pp][t][gs].
+    {
+      const int pl = threadIdx.x >> 5, sx = (threadIdx.x >> 2) & 7, pc = threadIdx.x & 3;
+      if (pl < CH && sx < nsb) {
+        const int pid = perm[min(c0 + pl, M - 1)];
+        const u32x2 sv = *reinterpret_cast<const u32x2*>(dsc + ((size_t)pid * nsb + sx) * 32 + 8 * pc);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(&st.sc[sx][0]);
+        const int pp = pc >> 1;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const int tt = 2 * (pc & 1) + (k >> 2), gs = k & 3;
+          dst[4 * (16 * gs + 4 * (pl & 3) + tt) + 2 * (pl >> 2) + pp] = (uint8_t)(sv[k >> 2] >> (8 * (k & 3)));
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies into LDS have landed
+    __syncthreads();
+
+    const int ng = min(NG, (M - c0 + 3) / 4);  // groups holding pairs (uniform)
+    f32x4_t acc[NG];
+#pragma unroll
+    for (int G = 0; G < NG; G++) acc[G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < QG_SB; i++) {
+      if (i < nsb) {
+        const int sa = (int)st.sc[i][lane];
+        f32x4_t cr[NG], cm[NG];
+#pragma unroll
+        for (int pp = 0; pp < 2; pp++) {
+          // scale/min bytes of planes 2 pp (byte 0) and 2 pp + 1 (byte 2)
+          const uint32_t rs = (pp ? rhi[i] : rlo[i]) >> (8 * (g & 1));
+          const uint32_t b0 = rs & 0xFFu, b1 = (rs >> 16) & 0xFFu;
+          const uint32_t mn = (rs >> 4) & 0x000F000Fu;  // the two mins in bytes 0 and 2
+          const uint32_t m0 = __builtin_amdgcn_perm(mn, mn, 0x00000000u), m1 = __builtin_amdgcn_perm(mn, mn, 0x02020202u);
+          i32x8_t B1, B2, B3;
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const uint32_t x0 = (q[i][j] >> (4 * pp)) & 0x03030303u, x1 = (q[i][j] >> (4 * pp + 2)) & 0x03030303u;
+            B1[j] = (int32_t)crumb_mul(x0, b0 & 3u);
+            B1[4 + j] = (int32_t)crumb_mul(x1, b1 & 3u);
+            B2[j] = (int32_t)crumb_mul(x0, (b0 >> 2) & 3u);
+            B2[4 + j] = (int32_t)crumb_mul(x1, (b1 >> 2) & 3u);
+            B3[j] = (int32_t)m0;
+            B3[4 + j] = (int32_t)m1;
+          }
+#pragma unroll
+          for (int G = 0; G < NG; G++) {
+            if (G < ng) {
+              const u32x4 lo = st.code[i][G][pp][0][lane], hi = st.code[i][G][pp][1][lane];
+              const i32x8_t A = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              // B scales 2^9, 2^11, 2^9: sl q, 4 sh q, m
+              cr[G] = mfma_sel(A, B1, pp ? cr[G] : z, 2 * G + pp, sa, 136);
+              cr[G] = mfma_sel(A, B2, cr[G], 2 * G + pp, sa, 138);
+              cm[G] = mfma_sel(A, B3, pp ? cm[G] : z, 2 * G + pp, sa, 136);
+            }
+          }
+        }
+        const float d = half_bits_f32(rdd[i]), dmin = half_bits_f32(rdd[i] >> 16);
+#pragma unroll
+        for (int G = 0; G < NG; G++)
+          if (G < ng)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[G][r] = __builtin_fmaf(d, cr[G][r], __builtin_fmaf(-dmin, cm[G][r], acc[G][r]));
+      }
+    }
+    // Lane (n, g): pair 4 G + g of the pass, weight row n0 + n.
+#pragma unroll
+    for (int G = 0; G < NG; G++) {
+      if (G < ng && c0 + 4 * G + g < M && n0 + n < P.rows) {
+        const float v = (acc[G][0] + acc[G][1]) + (acc[G][2] + acc[G][3]);
+        P.out[(size_t)po[G] * P.rows + n0 + n] = v * rwo[G];
+      }
+    }
+    // The B operands are rebuilt in every pass rather than kept for all of K (eight
+    // superblocks' worth would not fit in registers): the weight registers count as
+    // redefined here, so nothing derived from them is hoisted out of the loop.
+#pragma unroll
+    for (int i = 0; i < QG_SB; i++) asm volatile("" : "+v"(q[i]), "+v"(rlo[i]), "+v"(rhi[i]));
+  }
+}
+
 }  // namespace
 
 // K a multiple of 256 up to 2048, at most 6 slots.
@@ -265,6 +526,24 @@ hipError_t launch_down1_q2k(const Down1Params& p, hipStream_t s) {
   if (!down1_q2k_fits(p.rows, p.cols, p.top_k)) return hipErrorInvalidValue;
   dim3 g((unsigned)((p.rows + 15) / 16), (unsigned)(p.T > 1 ? p.T : 1)), b((unsigned)(64 * QD_KPARTS * p.top_k));
   hipLaunchKernelGGL(k_down1_q2k, g, b, 0, s, p);
+  return hipGetLastError();
+}
+
+
+bool dn_q2k_g_fits(int rows, int cols) { return rows > 0 && cols > 0 && cols % 256 == 0 && cols <= 256 * QG_SB; }
+
+size_t dn_q2k_g_digit_bytes(long pairs, int cols) { return (size_t)pairs * (size_t)cols * 4; }
+size_t dn_q2k_g_scale_bytes(long pairs, int cols) { return (size_t)pairs * (size_t)cols / 8; }
+
+hipError_t launch_dn_q2k_g(const GemvParams& p, int n_slots, uint8_t* dq, uint8_t* dsc, hipStream_t s) {
+  if (!dn_q2k_g_fits(p.rows, p.cols) || (uintptr_t)p.act % 16 || (uintptr_t)dq % 16 || (uintptr_t)dsc % 8)
+    return hipErrorInvalidValue;
+  const long nval8 = (long)p.T * p.top_k * (p.cols / 8);
+  if (nval8 <= 0 || nval8 > (long)0x7FFFFFFF - 255) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_q2k_digits, dim3((unsigned)((nval8 + 255) / 256)), dim3(256), 0, s, (const float*)p.act,
+                     (int)nval8, p.cols / 256, dq, dsc);
+  const dim3 g((unsigned)((p.rows + QG_ROWS - 1) / QG_ROWS), (unsigned)n_slots), b(64 * QG_WAVES);
+  hipLaunchKernelGGL(k_dn_q2k_g<1>, g, b, 0, s, p, dq, dsc);
   return hipGetLastError();
 }
 

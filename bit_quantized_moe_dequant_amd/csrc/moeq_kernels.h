@@ -131,6 +131,14 @@ bool down1_q2k_fits(int rows, int cols, int top_k);  // cols % 256 == 0, cols <=
 // Q2_K down + weighted combine of one token per grid row (p.T rows) on the
 // block-scaled FP8 matrix instruction.
 hipError_t launch_down1_q2k(const Down1Params& p, hipStream_t s);
+// Token-grouped Q2_K down (T > 1) on the block-scaled FP8 matrix instruction: h
+// (p.act, fp32 [pairs][cols], 16-byte aligned) to digit planes in dq / dsc
+// (dn_q2k_g_digit_bytes / dn_q2k_g_scale_bytes), then route-weighted partials
+// [pairs][rows] for the combine.
+bool dn_q2k_g_fits(int rows, int cols);  // cols % 256 == 0, cols <= 2048
+size_t dn_q2k_g_digit_bytes(long pairs, int cols);
+size_t dn_q2k_g_scale_bytes(long pairs, int cols);
+hipError_t launch_dn_q2k_g(const GemvParams& p, int n_slots, uint8_t* dq, uint8_t* dsc, hipStream_t s);
 // Token-grouped Q2_K down (T > 1) on the bf16 matrix instruction: route-weighted
 // partials [pairs][rows] for the combine.
 bool dn_q2k_fits(int rows, int cols, long pairs);
