@@ -301,6 +301,7 @@ __global__ __launch_bounds__(64 * QD_KPARTS * QD_SLOTS) QD_ATTR void k_down1_q2k
 constexpr int QG_WAVES = 4;
 constexpr int QG_ROWS = 16 * QG_WAVES;
 constexpr int QG_SB = 8;  // superblocks along K (K <= 2048)
+constexpr int QG_WLOADS = 3 * QG_SB;  // a wave's weight and record loads, fewest after merging
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -390,12 +391,63 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
   const int nsb = P.cols / 256;
   const int n0 = r0 + 16 * wave;
   const int rn = min(n0 + n, P.rows - 1);
-  // All of K for row rn: chunk g of each superblock, and the scale record dwords of
-  // chunk g's sub-blocks (planes 0, 1: dword 2 (g >> 1); planes 2, 3: the next) and
-  // d | dmin (superblocks past the end re-read the last and are not used).
+  // row rn of the expert: its data and its scale records
   const uint8_t* wrow = P.w[0].data + (size_t)e * P.w[0].estride + (size_t)rn * nsb * 64 + 16 * g;
   const uint32_t* srow =
       reinterpret_cast<const uint32_t*>(P.w[0].scales + (size_t)e * P.w[0].sestride + (size_t)rn * nsb * 20);
+  const int t = lane & 3, ip = (lane >> 2) & 3;  // this lane's A row: digit t of pair 4 G + ip
+  int pa[NG], po[NG];
+  float rwo[NG];
+  u32x2 sv = u32x2{0u, 0u};
+  const int pl = threadIdx.x >> 5, sx = (threadIdx.x >> 2) & 7, pc = threadIdx.x & 3;
+  const bool scl = pl < CH && sx < nsb;
+  // A pass's stage, first half: its pair ids and route weights, the digit codes copied
+  // straight into LDS (wave w copies the (pass w >> 1, half w & 1) pieces of every
+  // superblock and group, lane l = 16 g + 4 ip + t taking (pair 4 G + ip, group g,
+  // digit t)), and the loads of its scale codes (thread (pair pl, superblock sx, piece
+  // pc): 8 bytes [pp][t][gs]).
+  auto stage_issue = [&](int c0) {
+#pragma unroll
+    for (int G = 0; G < NG; G++) {
+      pa[G] = perm[min(c0 + 4 * G + ip, M - 1)];  // pairs past the last repeat it and are not stored
+      po[G] = perm[min(c0 + 4 * G + g, M - 1)];
+    }
+    const int pid = perm[min(c0 + pl, M - 1)];
+    const int pp = wave >> 1, half = wave & 1;
+#pragma unroll
+    for (int i = 0; i < QG_SB; i++)
+#pragma unroll
+      for (int G = 0; G < NG; G++)
+        if (i < nsb) {
+          const uint8_t* src = dq + ((size_t)pa[G] * nsb + i) * 1024 + (pp * 2 + half) * 256 + g * 64 + t * 16;
+          __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)&st.code[i][G][pp][half][0], 16, 0, 0);
+        }
+    if (scl) sv = *reinterpret_cast<const u32x2*>(dsc + ((size_t)pid * nsb + sx) * 32 + 8 * pc);
+#pragma unroll
+    for (int G = 0; G < NG; G++) rwo[G] = P.rw[po[G]];
+  };
+  // Second half: the scale codes into the lanes' bytes.
+  auto stage_store = [&]() {
+    if (scl) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>(&st.sc[sx][0]);
+      const int pp = pc >> 1;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int tt = 2 * (pc & 1) + (k >> 2), gs = k & 3;
+        dst[4 * (16 * gs + 4 * (pl & 3) + tt) + 2 * (pl >> 2) + pp] = (uint8_t)(sv[k >> 2] >> (8 * (k & 3)));
+      }
+    }
+  };
+
+  // The first pass's stage goes out before the weights, so that the wait for it
+  // below leaves the weight loads in flight and each superblock waits only for its
+  // own. All of K for row rn: chunk g of each superblock, and the scale record dwords
+  // of chunk g's sub-blocks (planes 0, 1: dword 2 (g >> 1); planes 2, 3: the next) and
+  // d | dmin (superblocks past the end re-read the last and are not used): QG_WLOADS
+  // loads, none of which can be merged (the record dwords are at lane-dependent
+  // offsets but for the first two, which at most become one).
+  stage_issue(0);
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 q[QG_SB];
   uint32_t rlo[QG_SB], rhi[QG_SB], rdd[QG_SB];
 #pragma unroll
@@ -408,49 +460,12 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const int t = lane & 3, ip = (lane >> 2) & 3;  // this lane's A row: digit t of pair 4 G + ip
-  for (int c0 = 0; c0 < M; c0 += CH) {
-    if (c0 > 0) __syncthreads();  // the previous pass has read the stage
-    int pa[NG], po[NG];
-    float rwo[NG];
-#pragma unroll
-    for (int G = 0; G < NG; G++) {
-      pa[G] = perm[min(c0 + 4 * G + ip, M - 1)];  // pairs past the last repeat it and are not stored
-      po[G] = perm[min(c0 + 4 * G + g, M - 1)];
-      rwo[G] = P.rw[po[G]];
-    }
-    // Digit codes: wave w copies the (pass w >> 1, half w & 1) pieces of every
-    // superblock and group, lane l = 16 g + 4 ip + t taking (pair 4 G + ip, group g,
-    // digit t).
-    {
-      const int pp = wave >> 1, half = wave & 1;
-#pragma unroll
-      for (int i = 0; i < QG_SB; i++)
-#pragma unroll
-        for (int G = 0; G < NG; G++)
-          if (i < nsb) {
-            const uint8_t* src = dq + ((size_t)pa[G] * nsb + i) * 1024 + (pp * 2 + half) * 256 + g * 64 + t * 16;
-            __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)&st.code[i][G][pp][half][0], 16, 0, 0);
-          }
-    }
-    // Scale codes: thread (pair pl, superblock sx, piece pc) moves 8 bytes [pp][t][gs].
-    {
-      const int pl = threadIdx.x >> 5, sx = (threadIdx.x >> 2) & 7, pc = threadIdx.x & 3;
-      if (pl < CH && sx < nsb) {
-        const int pid = perm[min(c0 + pl, M - 1)];
-        const u32x2 sv = *reinterpret_cast<const u32x2*>(dsc + ((size_t)pid * nsb + sx) * 32 + 8 * pc);
-        uint8_t* dst = reinterpret_cast<uint8_t*>(&st.sc[sx][0]);
-        const int pp = pc >> 1;
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const int tt = 2 * (pc & 1) + (k >> 2), gs = k & 3;
-          dst[4 * (16 * gs + 4 * (pl & 3) + tt) + 2 * (pl >> 2) + pp] = (uint8_t)(sv[k >> 2] >> (8 * (k & 3)));
-        }
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies into LDS have landed
-    __syncthreads();
-
+  // One pass over the stage (pairs c0 .. c0 + CH - 1). The empty asm at the top of
+  // each superblock ties everything derived from its weight registers (and the wait
+  // for them) to that superblock and pass: nothing is hoisted out of the passes
+  // (eight superblocks' B operands would not fit in registers) or ahead of the
+  // superblock's own loads.
+  auto pass = [&](int c0) {
     const int ng = min(NG, (M - c0 + 3) / 4);  // groups holding pairs (uniform)
     f32x4_t acc[NG];
 #pragma unroll
@@ -458,6 +473,7 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
 #pragma unroll
     for (int i = 0; i < QG_SB; i++) {
       if (i < nsb) {
+        asm volatile("" : "+v"(q[i]), "+v"(rlo[i]), "+v"(rhi[i]), "+v"(rdd[i]));
         const int sa = (int)st.sc[i][lane];
         f32x4_t cr[NG], cm[NG];
 #pragma unroll
@@ -507,11 +523,20 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
         P.out[(size_t)po[G] * P.rows + n0 + n] = v * rwo[G];
       }
     }
-    // The B operands are rebuilt in every pass rather than kept for all of K (eight
-    // superblocks' worth would not fit in registers): the weight registers count as
-    // redefined here, so nothing derived from them is hoisted out of the loop.
-#pragma unroll
-    for (int i = 0; i < QG_SB; i++) asm volatile("" : "+v"(q[i]), "+v"(rlo[i]), "+v"(rhi[i]));
+  };
+
+  stage_store();
+  // the first stage's copies, issued before the QG_WLOADS weight loads
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QG_WLOADS) : "memory");
+  __syncthreads();
+  pass(0);
+  for (int c0 = CH; c0 < M; c0 += CH) {
+    __syncthreads();  // the previous pass has read the stage
+    stage_issue(c0);
+    stage_store();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies into LDS have landed
+    __syncthreads();
+    pass(c0);
   }
 }
 
