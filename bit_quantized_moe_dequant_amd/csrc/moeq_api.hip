@@ -236,6 +236,14 @@ bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >=
 #ifndef MOEQ_MX4_BATCHED
 #define MOEQ_MX4_BATCHED 1
 #endif
+// NVFP4 gate/up off the direct path: on the same token-grouped kernel (one pair per
+// instruction) from this many pairs per touched expert, as grouped GEMVs below it.
+// NVFP4 + Q2_K layers at T = 32 / 64 / 256 (1.4 / 1.9 / 6 pairs): 429 / 652 / 1544 us
+// against 425 / 686 / 1661 us with the GEMVs; at T = 16 the direct path stays ahead
+// (256 against 268 us).
+#ifndef MOEQ_NV4_GROUPED_FROM
+#define MOEQ_NV4_GROUPED_FROM 1.5
+#endif
 
 // Scale plane read in 16-byte runs by the matrix-instruction kernels.
 bool scales16(const moeq_weight& w) {
@@ -306,9 +314,10 @@ int run_gate_up(const moeq_layer* L, const void* x, const int32_t* ids, int T, f
   if (T * L->top_k + 1 < slots) slots = T * L->top_k + 1;
   if (L->gate.fmt == MOEQ_FMT_IQ2_XXS && gu_iq2_fits(L->inter, L->hidden))
     return hip_rc(launch_gu_iq2(p, slots, (double)T * L->top_k >= MOEQ_IQ2_WIDE_FROM * L->n_experts, s));
-  if (MOEQ_MX4_BATCHED && L->gate.fmt == MOEQ_FMT_MXFP4 && gu_mx4_g_fits(L->inter, L->hidden) && scales16(L->gate) &&
-      scales16(L->up))
-    return hip_rc(launch_gu_mx4_g(p, slots, s));
+  const bool fp4_g = (MOEQ_MX4_BATCHED && L->gate.fmt == MOEQ_FMT_MXFP4) ||
+                     (L->gate.fmt == MOEQ_FMT_NVFP4 && pairs_per_expert(L, T) >= MOEQ_NV4_GROUPED_FROM);
+  if (fp4_g && gu_mx4_g_fits(L->inter, L->hidden) && scales16(L->gate) && scales16(L->up))
+    return hip_rc(launch_gu_fp4_g(L->gate.fmt, p, slots, s));
   return hip_rc(launch_gemv(L->gate.fmt, EPI_SWIGLU, p, slots, grouped_wide(L, T) ? 4 : 1, s, ev));
 }
 

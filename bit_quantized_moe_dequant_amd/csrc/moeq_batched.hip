@@ -24,6 +24,15 @@
 // Gate/up writes h[pair][row] = silu(g) * u; down writes route-weighted partials
 // [pair][row] for the slot-order combine. The bucket of out-of-range ids writes
 // zeros.
+//
+// NVFP4 gate/up (e2m1 codes, an E4M3 scale per 16 along K, an fp32 scale_2 per
+// expert tensor: DeepSeek V4 Flash - REAP K180 Mixed NVFP4 card, section "NVFP4:
+// lossless MXFP4->NVFP4 conversion") runs in the same kernel with the single-token
+// kernel's operand layout: its block scale is neither a power of two nor 32 wide,
+// so B takes scale 1 and each instruction serves one pair, A row 8 t + d carrying
+// term t of x on 16-block d of the step (zeros elsewhere); the lane holding output
+// rows 4 q .. 4 q + 3 multiplies them by their blocks' E4M3 scales (one 32-bit word
+// of the row's scale plane, converted once per step for all pairs of the tile).
 #include <hip/hip_runtime.h>
 
 #include "moeq_device.h"
@@ -59,7 +68,14 @@ struct GuStage {
   uint8_t sc[2][GU_TILE * GU_KMAX / 32];
 };
 
-__global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
+template <int FMT>
+__global__ __launch_bounds__(GU_NT) void k_gu_fp4_g(GemvParams P) {
+  constexpr bool NV = FMT == FMT_NVFP4;
+  constexpr int SPB = NV ? 8 : 4;            // scale bytes per row and 128-wide step
+  constexpr int NSB = GU_STEPS * SPB / 16;   // 16-byte scale runs per wave and row
+  // pairs per staged tile (NVFP4: one pair per instruction; a tile of four keeps
+  // its staging registers small enough for two waves per SIMD)
+  constexpr int TILE = NV ? GU_TILE / 2 : GU_TILE;
   __shared__ GuStage st;
   __shared__ float red[GU_WAVES][2][GU_TILE][16];
 
@@ -86,13 +102,13 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
   const int my = max(0, min(spw, nsteps - s0));
   const int n = lane & 15, g = lane >> 4;
   const int rn = min(n0 + n, P.rows - 1);
-  constexpr int XC = GU_TILE * GU_KMAX / 16 / GU_NT;  // chunk loads per thread per tile, at most
+  constexpr int XC = TILE * GU_KMAX / 16 / GU_NT;  // chunk loads per thread per tile, at most
 
   // A tile's tokens -> two E4M3 terms in LDS: stage_load issues the loads,
   // stage_convert converts and stores (it waits only for those loads).
   u32x4 xa[XC], xb[XC];
   auto stage_load = [&](int m0) {
-    const int tn = min(GU_TILE, M - m0);
+    const int tn = min(TILE, M - m0);
     const int nc = (tn * cpt + GU_NT - 1) / GU_NT;  // uniform
 #pragma unroll
     for (int j = 0; j < XC; j++) {
@@ -108,7 +124,7 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
     }
   };
   auto stage_convert = [&](int m0) {
-    const int tn = min(GU_TILE, M - m0);
+    const int tn = min(TILE, M - m0);
     const int nc = (tn * cpt + GU_NT - 1) / GU_NT;  // uniform
 #pragma unroll
     for (int j = 0; j < XC; j++) {
@@ -133,13 +149,14 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
   stage_load(0);
   __builtin_amdgcn_sched_barrier(0);
   u32x4 q[2][GU_STEPS];
-  u32x4 sbv4[2][GU_STEPS / 4];
+  u32x4 sbv4[2][NSB];
+  const float s2g = NV ? P.w[0].scale2[e] : 1.f, s2u = NV ? P.w[1].scale2[e] : 1.f;
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const uint8_t* wd = P.w[mt].data + (size_t)e * P.w[mt].estride + (size_t)rn * (K / 2);
-    const uint8_t* ws = P.w[mt].scales + (size_t)e * P.w[mt].sestride + (size_t)rn * (K / 32);
+    const uint8_t* ws = P.w[mt].scales + (size_t)e * P.w[mt].sestride + (size_t)rn * (K / 128 * SPB);
 #pragma unroll
-    for (int j = 0; j < GU_STEPS / 4; j++) sbv4[mt][j] = ld16(ws + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
+    for (int j = 0; j < NSB; j++) sbv4[mt][j] = ld16(ws + (size_t)min(SPB * s0 + 16 * j, SPB * nsteps - 16));
 #pragma unroll
     for (int i = 0; i < GU_STEPS; i++)
       q[mt][i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
@@ -148,45 +165,99 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
   stage_convert(0);
 
   const int pj = n >> 1, term = n & 1;  // this lane's A row: pair pj of the tile, its term
-  for (int m0 = 0; m0 < M; m0 += GU_TILE) {
-    const int tn = min(GU_TILE, M - m0);
+  for (int m0 = 0; m0 < M; m0 += TILE) {
+    const int tn = min(TILE, M - m0);
     if (m0 > 0) {
       __syncthreads();  // the previous tile has read the staging and the partials
       stage_load(m0);
       stage_convert(m0);
     }
     __syncthreads();
-    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (!NV) {
+      f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int i = 0; i < GU_STEPS; i++) {
-      if (i < my) {
-        const int s = s0 + i;
-        u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
-        int sa = 0;
-        if (pj < tn) {
-          const int off = pj * K + 128 * s + 16 * g;
-          a0 = *reinterpret_cast<const u32x4*>(&st.code[term][off]);
-          a1 = *reinterpret_cast<const u32x4*>(&st.code[term][off + 64]);
-          sa = st.sc[term][(pj * K) / 32 + 4 * s + g];
+      for (int i = 0; i < GU_STEPS; i++) {
+        if (i < my) {
+          const int s = s0 + i;
+          u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
+          int sa = 0;
+          if (pj < tn) {
+            const int off = pj * K + 128 * s + 16 * g;
+            a0 = *reinterpret_cast<const u32x4*>(&st.code[term][off]);
+            a1 = *reinterpret_cast<const u32x4*>(&st.code[term][off + 64]);
+            sa = st.sc[term][(pj * K) / 32 + 4 * s + g];
+          }
+          const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int mt = 0; mt < 2; mt++) {
+            const i32x8_t bv =
+                __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
+            const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
+          }
         }
-        const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      // lane (column n, g): registers 0, 1 = pair 2g (its terms), 2, 3 = pair 2g + 1
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        red[wave][mt][2 * g][n] = acc[mt][0] + acc[mt][1];
+        red[wave][mt][2 * g + 1][n] = acc[mt][2] + acc[mt][3];
+      }
+    } else {
+      // A row n = 8 t + d: term t of the pair on block d, whose 16 bytes are lane group
+      // d & 3's low (d < 4) or high half; the scale is term t's e8m0 of the lane
+      // group's own K-block (it multiplies zeros elsewhere).
+      const int t = n >> 3, d = n & 7;
+      // Pair by pair (one instruction per pair and step), so that only one pair's
+      // sums are live; the scale words are converted again for each pair.
+#pragma unroll 1
+      for (int j = 0; j < tn; j++) {
+        float accn[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < GU_STEPS; i++) {
+          if (i < my) {
+            const int s = s0 + i;
+            u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
+            const int sa = st.sc[t][(j * K) / 32 + 4 * s + g];
+            if ((d & 3) == g) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(&st.code[t][j * K + 128 * s + 16 * d]);
+              if (d < 4) a0 = v;
+              else a1 = v;
+            }
+            const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++) {
+              const i32x8_t bv =
+                  __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
+              const f32x4_t c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  av, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, sa, 0, 127);
+              // E4M3 scales of blocks 4 (g & 1) + r of step s for row n: one word
+              const uint32_t sw = sbv4[mt][i >> 1][2 * (i & 1) + (g & 1)];
+              const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+              const f32x2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, true);
+              float a = accn[mt];
+              a = __builtin_fmaf(s01[0], c[0], a);
+              a = __builtin_fmaf(s01[1], c[1], a);
+              a = __builtin_fmaf(s23[0], c[2], a);
+              accn[mt] = __builtin_fmaf(s23[1], c[3], a);
+            }
+          }
+          // one step at a time: unbounded overlap of the steps' results would take
+          // the registers of a second wave per SIMD
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the four lane groups of column n: both terms, both halves of each step
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
-          const i32x8_t bv =
-              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q[mt][i], q[mt][i], 0, 1, 2, 3, -1, -1, -1, -1));
-          const int sbv = (int)(sbv4[mt][i >> 2][i & 3] >> (8 * g));
-          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 4, 0, sa, 0, sbv);
+          float a = accn[mt];
+          a += __shfl_xor(a, 16, 64);
+          a += __shfl_xor(a, 32, 64);
+          if (lane < 16) red[wave][mt][j][n] = a;
         }
       }
     }
-    // lane (column n, g): registers 0, 1 = pair 2g (its terms), 2, 3 = pair 2g + 1
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      red[wave][mt][2 * g][n] = acc[mt][0] + acc[mt][1];
-      red[wave][mt][2 * g + 1][n] = acc[mt][2] + acc[mt][3];
-    }
     __syncthreads();
-    if (threadIdx.x < 16 * GU_TILE) {
+    if (threadIdx.x < 16 * TILE) {
       const int j = threadIdx.x >> 4, col = threadIdx.x & 15;
       const int r = n0 + col;
       if (j < tn && r < P.rows) {
@@ -196,7 +267,7 @@ __global__ __launch_bounds__(GU_NT) void k_gu_mx4_g(GemvParams P) {
           gs += red[w][0][j][col];
           us += red[w][1][j][col];
         }
-        P.out[(size_t)P.route.perm()[pstart + m0 + j] * P.rows + r] = silu_mul(gs, us);
+        P.out[(size_t)P.route.perm()[pstart + m0 + j] * P.rows + r] = silu_mul(gs * s2g, us * s2u);
       }
     }
   }
@@ -343,9 +414,13 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
 bool gu_mx4_g_fits(int rows, int cols) { return rows > 0 && cols > 0 && cols % 512 == 0 && cols <= GU_KMAX; }
 bool dn_mx4_g_fits(int rows, int cols) { return rows > 0 && cols > 0 && cols % 512 == 0 && cols <= DN_KMAX; }
 
-hipError_t launch_gu_mx4_g(const GemvParams& p, int n_slots, hipStream_t s) {
-  if (!gu_mx4_g_fits(p.rows, p.cols)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gu_mx4_g, dim3((unsigned)((p.rows + 15) / 16), (unsigned)n_slots), dim3(GU_NT), 0, s, p);
+hipError_t launch_gu_fp4_g(int fmt, const GemvParams& p, int n_slots, hipStream_t s) {
+  if (!gu_mx4_g_fits(p.rows, p.cols) || (fmt != FMT_MXFP4 && fmt != FMT_NVFP4)) return hipErrorInvalidValue;
+  const dim3 g((unsigned)((p.rows + 15) / 16), (unsigned)n_slots);
+  if (fmt == FMT_NVFP4)
+    hipLaunchKernelGGL(k_gu_fp4_g<FMT_NVFP4>, g, dim3(GU_NT), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_gu_fp4_g<FMT_MXFP4>, g, dim3(GU_NT), 0, s, p);
   return hipGetLastError();
 }
 

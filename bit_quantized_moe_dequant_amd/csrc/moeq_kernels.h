@@ -157,7 +157,7 @@ hipError_t launch_linear_fp8(const LinearParams& p, hipStream_t s);
 // matrix instruction, each routed expert's weights read once per step.
 bool gu_mx4_g_fits(int rows, int cols);  // cols % 512 == 0, cols <= 4096
 bool dn_mx4_g_fits(int rows, int cols);  // cols % 512 == 0, cols <= 2048
-hipError_t launch_gu_mx4_g(const GemvParams& p, int n_slots, hipStream_t s);
+hipError_t launch_gu_fp4_g(int fmt, const GemvParams& p, int n_slots, hipStream_t s);  // MXFP4 or NVFP4
 hipError_t launch_dn_mx4_g(const GemvParams& p, int n_slots, hipStream_t s);
 
 bool linear_mx8_fits(int fmt, int rows, int cols);  // rows % 16, cols % 128 (pre-stored: % 512), cols <= 8192

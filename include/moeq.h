@@ -16,9 +16,10 @@
  * VALU (dequantize + GEMV). Up to 32 tokens (16 for NVFP4 gate/up; Q2_K down below
  * 1.06 pairs per touched expert) these kernels run over every (token, slot) pair
  * with no routing step; beyond, each routed expert is read once per step for all
- * of its tokens (MXFP4 and the Q2_K down on the block-scaled instruction, Q2_K's
- * sub-block scale and min folded into the FP8 operand; IQ2_XXS gate/up and down
- * decoding once per 16-token tile for the bf16 matrix instruction). At prefill with MXFP4 weights it is a token-grouped GEMM
+ * of its tokens (MXFP4, the NVFP4 gate/up and the Q2_K down on the block-scaled
+ * instruction, Q2_K's sub-block scale and min folded into the FP8 operand; IQ2_XXS
+ * gate/up and down decoding once per 16-token tile for the bf16 matrix
+ * instruction). At prefill with MXFP4 weights it is a token-grouped GEMM
  * on the block-scaled FP4 matrix instructions, with activations quantised to
  * MXFP8 (fp4 weights times E4M3 activations: DeepSeekv4 Flash for 1x Spark forum
  * thread, second post). The decode paths agree with the exact layer to the

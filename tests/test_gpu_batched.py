@@ -1,8 +1,10 @@
-"""Batched MXFP4 decode (T > 1) on the block-scaled matrix instruction against the
-CPU oracle. Up to 32 tokens the single-token kernels run over every (token, slot)
-pair; beyond, the grouped kernels take each routed expert's pairs in tiles of
-eight (gate/up) and five (down). Cases: experts with several tiles of pairs,
-out-of-range ids on both paths, and the full DeepSeek-V4-Flash-shaped layer at
+"""Batched MXFP4 and NVFP4 decode (T > 1) on the block-scaled matrix instruction
+against the CPU oracle. Up to 32 tokens (16 for the NVFP4 gate/up) the
+single-token kernels run over every (token, slot) pair; beyond, the grouped
+kernels take each routed expert's pairs in tiles of eight (MXFP4 gate/up), four
+(NVFP4 gate/up, one pair per instruction) and five (MXFP4 down). Cases: experts
+with several tiles of pairs, K of 1024 and 4096 (one and eight steps per wave),
+out-of-range ids on both paths, and the full DeepSeek-V4-Flash-shaped layers at
 16 and 64 tokens (co-scheduled decode sessions)."""
 import sys
 
@@ -79,6 +81,73 @@ def test_batched_mxfp4_out_of_range_id(T):
 def test_batched_mxfp4_full_layer(T, sample):
     say("batched mxfp4 full layer", T)
     wl = workloads.WORKLOADS["mxfp4_layer"]
+    layer = workloads.build_layer(mq, wl.spec)
+    ids, rw = synth.uniform_routing(wl.spec.seed + 900 + T, T, 256, 6)
+    x = synth.activations_bf16(wl.spec.seed + 901 + T, T, 4096)
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    y = mq.expert_forward(layer, x_tensor(x), cuda(ids), cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) == 0
+    ref, _ = moe.moe_layer(x[sample], ids[sample], rw[sample], oracle_weight_fn(wl.spec))
+    err = rel_err(y[sample], ref)
+    say("err", err)
+    assert err < TOL
+    del layer
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("H,T,E,K", [(1024, 17, 8, 6), (1024, 40, 8, 6), (1024, 22, 2, 1), (4096, 24, 8, 6),
+                                     (1024, 33, 64, 6), (1024, 20, 256, 6)])
+def test_batched_nvfp4_gate_up_tiles(H, T, E, K):
+    """NVFP4 gate/up on the grouped kernel (from 17 tokens and 1.5 pairs per touched
+    expert): 12.75 and 30 pairs per expert (tiles of four, the last partial), two
+    experts of 11 pairs, hidden 4096 (eight K steps per wave), about 3.2 pairs per
+    expert over 64 experts; and the grouped GEMV below 1.5 pairs (T = 20 over 256
+    experts)."""
+    say("batched nvfp4", H, T, E, K)
+    spec = workloads.LayerSpec(H, 512, E, K, mq.FMT_NVFP4, mq.FMT_MXFP4, seed=6300 + T + E + H)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, E, K)
+    x = synth.activations_bf16(spec.seed + 1, T, H)
+    ref_y, ref_h = moe.moe_layer(x, ids, rw, oracle_weight_fn(spec))
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    xt, it, rt = x_tensor(x), cuda(ids), cuda(rw)
+    y = mq.expert_forward(layer, xt, it, rt, ws=ws).cpu().numpy()
+    mq.route(layer, it, ws=ws)
+    h = mq.gate_up(layer, xt, it, ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) == 0
+    eh, ey = rel_err(h, ref_h), rel_err(y, ref_y)
+    say("h err", eh, "y err", ey)
+    assert eh < TOL and ey < TOL
+
+
+def test_batched_nvfp4_out_of_range_id():
+    say("batched nvfp4 bad id")
+    E, K, T = 8, 6, 40
+    spec = workloads.LayerSpec(1024, 512, E, K, mq.FMT_NVFP4, mq.FMT_MXFP4, seed=6400)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, E, K)
+    bad = ids.copy()
+    bad[3, 2] = -1
+    bad[7, 5] = E
+    rw0 = rw.copy()
+    rw0[3, 2] = rw0[7, 5] = 0.0
+    x = synth.activations_bf16(spec.seed + 1, T, 1024)
+    ref_y, _ = moe.moe_layer(x, ids, rw0, oracle_weight_fn(spec))
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    y = mq.expert_forward(layer, x_tensor(x), cuda(bad), cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    assert rel_err(y, ref_y) < TOL
+
+
+@pytest.mark.parametrize("T,sample", [(64, [0, 31, 63])])
+def test_batched_nvfp4_q2k_full_layer(T, sample):
+    """The NVFP4 + Q2_K layer of the DeepSeek-V4-Flash shape at 64 co-scheduled
+    tokens: grouped NVFP4 gate/up and grouped Q2_K down."""
+    say("batched nvfp4 + q2k full layer", T)
+    wl = workloads.WORKLOADS["nvfp4_q2k"]
     layer = workloads.build_layer(mq, wl.spec)
     ids, rw = synth.uniform_routing(wl.spec.seed + 900 + T, T, 256, 6)
     x = synth.activations_bf16(wl.spec.seed + 901 + T, T, 4096)
