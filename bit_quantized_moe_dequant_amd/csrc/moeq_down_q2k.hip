@@ -345,6 +345,26 @@ __global__ __launch_bounds__(256) void k_q2k_digits(const float* __restrict__ h,
   for (int t = 0; t < 4; t++) *reinterpret_cast<u32x2*>(cb + 16 * t) = u32x2{w[t][0], w[t][1]};
 }
 
+// The three B operands of pass pp (planes 2 pp and 2 pp + 1 of the lane's chunk q):
+// sl q, sh q and m as E4M3 codes 0 .. 15, from rs = the scale/min bytes of the two
+// planes' sub-blocks in bytes 0 and 2.
+__device__ __forceinline__ void qg_operands(const u32x4& q, uint32_t rs, int pp, i32x8_t& B1, i32x8_t& B2,
+                                            i32x8_t& B3) {
+  const uint32_t b0 = rs & 0xFFu, b1 = (rs >> 16) & 0xFFu;
+  const uint32_t mn = (rs >> 4) & 0x000F000Fu;  // the two mins in bytes 0 and 2
+  const uint32_t m0 = __builtin_amdgcn_perm(mn, mn, 0x00000000u), m1 = __builtin_amdgcn_perm(mn, mn, 0x02020202u);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const uint32_t x0 = (q[j] >> (4 * pp)) & 0x03030303u, x1 = (q[j] >> (4 * pp + 2)) & 0x03030303u;
+    B1[j] = (int32_t)crumb_mul(x0, b0 & 3u);
+    B1[4 + j] = (int32_t)crumb_mul(x1, b1 & 3u);
+    B2[j] = (int32_t)crumb_mul(x0, (b0 >> 2) & 3u);
+    B2[4 + j] = (int32_t)crumb_mul(x1, (b1 >> 2) & 3u);
+    B3[j] = (int32_t)m0;
+    B3[4 + j] = (int32_t)m1;
+  }
+}
+
 // The instruction with A's scale taken from byte sel of sa (sel a constant once the
 // callers' loops are unrolled).
 __device__ __forceinline__ f32x4_t mfma_sel(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c, int sel, int sa,
@@ -478,22 +498,8 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
         f32x4_t cr[NG], cm[NG];
 #pragma unroll
         for (int pp = 0; pp < 2; pp++) {
-          // scale/min bytes of planes 2 pp (byte 0) and 2 pp + 1 (byte 2)
-          const uint32_t rs = (pp ? rhi[i] : rlo[i]) >> (8 * (g & 1));
-          const uint32_t b0 = rs & 0xFFu, b1 = (rs >> 16) & 0xFFu;
-          const uint32_t mn = (rs >> 4) & 0x000F000Fu;  // the two mins in bytes 0 and 2
-          const uint32_t m0 = __builtin_amdgcn_perm(mn, mn, 0x00000000u), m1 = __builtin_amdgcn_perm(mn, mn, 0x02020202u);
           i32x8_t B1, B2, B3;
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const uint32_t x0 = (q[i][j] >> (4 * pp)) & 0x03030303u, x1 = (q[i][j] >> (4 * pp + 2)) & 0x03030303u;
-            B1[j] = (int32_t)crumb_mul(x0, b0 & 3u);
-            B1[4 + j] = (int32_t)crumb_mul(x1, b1 & 3u);
-            B2[j] = (int32_t)crumb_mul(x0, (b0 >> 2) & 3u);
-            B2[4 + j] = (int32_t)crumb_mul(x1, (b1 >> 2) & 3u);
-            B3[j] = (int32_t)m0;
-            B3[4 + j] = (int32_t)m1;
-          }
+          qg_operands(q[i], (pp ? rhi[i] : rlo[i]) >> (8 * (g & 1)), pp, B1, B2, B3);
 #pragma unroll
           for (int G = 0; G < NG; G++) {
             if (G < ng) {

@@ -1,10 +1,9 @@
 """Token-grouped Q2_K down (T > 1) on the block-scaled FP8 matrix instruction against
 the CPU oracle: each expert's weights read once for all of its pairs, h as four
 digits per 32-value block made once per pair. The layer shapes are chosen so the
-grouped path runs (at least 2.5 expected pairs per touched expert); they cover one
-and two groups of four pairs per pass, experts with more pairs than one pass holds
-(further passes over the same weight registers), one, three and eight superblocks
-along K, a partial last 64-row tile, out-of-range ids, h with one outlier per
+grouped path runs; they cover experts of one pass of four pairs and of many passes
+over the same weight registers (up to nine), one, three and eight superblocks along
+K, a partial last 64-row tile, out-of-range ids, h with one outlier per
 32-block, and the full DeepSeek-V4-Flash down at T = 256 (sampled tokens). The bound
 is much tighter than the projection tolerance: four digits keep 19 bits of h
 relative to each block's maximum and every product is exact."""
@@ -43,7 +42,9 @@ def bucket_sizes(ids, E):
     (1024, 256, 16, 2, 24),    # one superblock; about 3 pairs per expert: one group per pass
     (544, 768, 16, 2, 40),     # three superblocks, partial 64-row tile, up to 9+ pairs (passes)
     (1024, 2048, 8, 6, 8),     # eight superblocks, 6 pairs per expert: two groups per pass
-    (512, 512, 8, 6, 48),      # 36 pairs per expert: several two-group passes
+    (512, 512, 8, 6, 48),      # 36 pairs per expert: nine passes
+    (512, 256, 2, 1, 40),      # one superblock, 20 pairs per expert: five passes
+    (1024, 2048, 4, 4, 20),    # eight superblocks, 20 pairs per expert
 ])
 def test_q2k_grouped_down_matches_oracle(H, I, E, K, T):
     say("q2k grouped down", H, I, E, K, T)
