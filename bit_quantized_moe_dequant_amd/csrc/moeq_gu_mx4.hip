@@ -51,10 +51,20 @@ constexpr int MX_KMAX = 128 * MX_WAVES * MX_STEPS;    // 4096
 #ifndef MOEQ_MX_DEPTH
 #define MOEQ_MX_DEPTH 8
 #endif
+// NVFP4 gate/up K steps in flight per wave for a single token (its six slots'
+// work-groups fit the chip in one round): its steps carry the block-scale
+// arithmetic, and loads interleaved with them measured faster (bs=1 NVFP4 + Q2_K
+// layer: 22.41 us at 2, 22.51 at 3, 22.93 at 8, 23.3 at 1). Over several tokens
+// (more work-groups than fit at once) all steps' loads first is faster (T = 16:
+// 252 - 255 against 260 - 262 us at 2), as it is for MXFP4 at any T (bs=1: 19.5 us
+// at 8, 20.05 - 20.27 at 2 - 6).
+#ifndef MOEQ_NV_DEPTH
+#define MOEQ_NV_DEPTH 2
+#endif
 #ifndef MOEQ_DM_DEPTH
 #define MOEQ_DM_DEPTH 8
 #endif
-constexpr int MX_DEPTH = MOEQ_MX_DEPTH;  // gate/up K steps in flight per wave
+constexpr int MX_DEPTH = MOEQ_MX_DEPTH;  // gate/up K steps in flight per wave (MXFP4)
 constexpr int DM_DEPTH = MOEQ_DM_DEPTH;  // down K steps in flight per wave
 
 // e8m0 exponent of a 32-block with maximum a: the smallest 2^e with a / 2^e <= 448
@@ -95,7 +105,7 @@ struct MxStage {
 // d < 4. (For MXFP4 the K-block of the scale is what matters and the rows are just
 // the terms.)
 
-template <int FMT>
+template <int FMT, int DEPTH>  // DEPTH: K steps in flight per wave
 __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
   constexpr bool NV = FMT == FMT_NVFP4;
   __shared__ MxStage st;
@@ -156,7 +166,7 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
     for (int mt = 0; mt < 2; mt++) q[mt][i] = ld16(wd[mt] + (size_t)s * 64 + 16 * g);
   };
 #pragma unroll
-  for (int i = 0; i < MX_DEPTH; i++) load_step(i);
+  for (int i = 0; i < DEPTH; i++) load_step(i);
   __builtin_amdgcn_sched_barrier(0);
 
   // x -> hi/lo E4M3 codes and per-32 scales in LDS.
@@ -211,8 +221,8 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
   float accn[2] = {0.f, 0.f};  // NVFP4: this lane's scaled block sums
 #pragma unroll
   for (int i = 0; i < MX_STEPS; i++) {
-    if constexpr (MX_DEPTH < MX_STEPS) {
-      if (i + MX_DEPTH < MX_STEPS) load_step(i + MX_DEPTH);  // keep MX_DEPTH steps in flight
+    if constexpr (DEPTH < MX_STEPS) {
+      if (i + DEPTH < MX_STEPS) load_step(i + DEPTH);  // keep DEPTH steps in flight
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i < my_steps) {
@@ -466,7 +476,9 @@ hipError_t launch_down1_mx4(const Down1Params& p, hipStream_t s) {
 hipError_t launch_gu1_fp4(int fmt, const GemvParams& p, int n_slots, hipStream_t s, const LaunchEvents* ev) {
   if (!gu1_mx4_fits(p.rows, p.cols) || (fmt != FMT_MXFP4 && fmt != FMT_NVFP4)) return hipErrorInvalidValue;
   dim3 g((unsigned)((p.rows + 15) / 16), (unsigned)n_slots), b(64 * MX_WAVES);
-  auto k = fmt == FMT_NVFP4 ? k_gu1_fp4<FMT_NVFP4> : k_gu1_fp4<FMT_MXFP4>;
+  auto k = fmt == FMT_MXFP4 ? k_gu1_fp4<FMT_MXFP4, MX_DEPTH>
+           : n_slots <= 8    ? k_gu1_fp4<FMT_NVFP4, MOEQ_NV_DEPTH>
+                             : k_gu1_fp4<FMT_NVFP4, MX_DEPTH>;
   if (ev) hipExtLaunchKernelGGL(k, g, b, 0, s, ev->start, ev->stop, 0, p);
   else hipLaunchKernelGGL(k, g, b, 0, s, p);
   return hipGetLastError();
