@@ -224,7 +224,7 @@ bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >=
 // (decode once per 16 tokens) from MOEQ_DN_Q2K_FROM pairs. The FP8 kernel was
 // faster at every load measured: IQ2_XXS + Q2_K layers at T = 64 / 256 / 2048 (2,
 // 6 and 48 pairs) took 782 / 1201 / 3448 us against 1108 (direct) / 1423 / 3768 us
-// (bf16). The bf16 kernel stays for h that is not 16-byte aligned.
+// (bf16). The bf16 kernel stays for intermediate sizes above 2048.
 #ifndef MOEQ_DN_Q2K_FROM
 #define MOEQ_DN_Q2K_FROM 2.5
 #endif

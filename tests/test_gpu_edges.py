@@ -237,3 +237,50 @@ def test_iq2_direct_few_tokens(T):
     eh, ey = rel_err(h[ok], ref_h[ok]), rel_err(y, ref_y)
     say("h err", eh, "y err", ey)
     assert eh < TOL and ey < TOL
+
+
+@pytest.mark.parametrize("fmt_dn,T", [(mq.FMT_Q2_K, 1), (mq.FMT_Q2_K, 8), (mq.FMT_MXFP4, 8)])
+def test_down_rejects_unaligned_h(fmt_dn, T):
+    """h 4 bytes past a 16-byte boundary is refused before any launch (the down
+    kernels read h 16 bytes at a time; the C ABI documents 16-byte alignment)."""
+    say("down unaligned h", fmt_dn, T)
+    spec = workloads.LayerSpec(1024, 512, 8, 6, mq.FMT_NVFP4, fmt_dn, seed=5900 + T + fmt_dn)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, 8, 6)
+    buf = torch.zeros(T * 6 * 512 + 4, dtype=torch.float32, device="cuda")
+    ht = buf[1:1 + T * 6 * 512].view(T, 6, 512)
+    assert ht.data_ptr() % 16 == 4
+    ws = layer.workspace(T)
+    it = cuda(ids)
+    if T > 1:
+        mq.route(layer, it, ws=ws)
+    with pytest.raises(mq.MoeqError):
+        mq.down(layer, ht, it, cuda(rw), ws=ws)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,E", [(1, 64), (3, 64), (8, 8)])
+def test_q2k_down_intermediate_beyond_2048(T, E):
+    """A Q2_K down with intermediate 2560 (ten superblocks, past the FP8 kernels'
+    2048): the dequantize + GEMV at one token, GEMV partials at three tokens over 64
+    experts, and the bf16 matrix-instruction grouped down at six pairs per expert."""
+    say("q2k down I=2560", T, E)
+    K, I = 6, 2560
+    spec = workloads.LayerSpec(512, I, E, K, mq.FMT_NVFP4, mq.FMT_Q2_K, seed=5950 + T + E)
+    layer = workloads.build_layer(mq, spec)
+    ids, rw = synth.uniform_routing(spec.seed, T, E, K)
+    rng = np.random.default_rng(spec.seed)
+    h = (moe.silu(rng.standard_normal((T, K, I)) * 2.0) * rng.standard_normal((T, K, I)) * 2.0).astype(np.float32)
+    ws = layer.workspace(T)
+    mq.check_device_error(ws)
+    it = cuda(ids)
+    if T > 1:
+        mq.route(layer, it, ws=ws)
+    y = mq.down(layer, cuda(h), it, cuda(rw), ws=ws).cpu().numpy()
+    assert mq.check_device_error(ws) == 0
+    wfn = oracle_weight_fn(spec)
+    ref = np.array([sum(float(rw[t, k]) * (wfn(moe.DOWN, int(ids[t, k])) @ h[t, k].astype(np.float64))
+                        for k in range(K)) for t in range(T)])
+    e = rel_err(y, ref)
+    say("err", e)
+    assert e < TOL
