@@ -21,11 +21,12 @@
 //
 // Work: a work-group is (one routed expert, 64 weight rows); each of its four waves
 // takes 16 rows of the gate and of the up matrix (SwiGLU is then lane-local).
-// Superblocks (256 K) stream through two register buffers: the next superblock's
-// loads are issued before the current one is computed. The decode is bound by
-// VALU and by the random 16-byte codebook reads from LDS together (four waves per
-// SIMD with half-superblock buffers ran slower than two with whole ones). Token lanes past the
-// expert's last token read that token again (same addresses) and are not stored.
+// Superblocks (256 K) stream through two buffers (weight bytes in LDS, the rest in
+// registers): the next superblock's loads are issued before the current one is
+// computed. Each weight byte is loaded by one lane only (see sb_rows_issue); with
+// four lanes per row loading the whole row the kernel was bound by those loads.
+// Token lanes past the expert's last token read that token again (same
+// addresses) and are not stored.
 #include <hip/hip_runtime.h>
 
 #include "moeq_device.h"
@@ -41,14 +42,29 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int GI_WAVES = 4;
 constexpr int GI_ROWS = 16 * GI_WAVES;  // weight rows per work-group
 
-// One superblock (256 K) of one wave: the 64 bytes of sub-block data and the fp16
-// d of row n for both matrices, and the 16-token activation slices (8 bf16 per
-// sub-block per lane).
+// One superblock (256 K) of one wave: the fp16 d of row n for both matrices and
+// the 16-token activation slices (8 bf16 per sub-block per lane) in registers; the
+// 64 bytes of sub-block data of each row in LDS (below).
 struct GiBuf {
-  u32x4 w[2][4];
   uint32_t d[2];
   u32x4 x[8];
 };
+
+// A superblock's weight bytes of a wave's 16 rows go through LDS. Every lane needs
+// all 64 bytes of its row, but the four lanes of a row loading the same bytes made
+// the kernel wait on its loads: four times the address work for the same lines
+// (762 against 534 us per IQ2_XXS + Q2_K layer at T = 64, uniform routing). So lane
+// (n, g) loads only bytes [16g, 16g + 16) of row n, straight into LDS, where the
+// load puts lane l's 16 bytes at the wave's base + 16 l; each lane then reads the
+// four pieces of its row back.
+typedef __attribute__((address_space(3))) void gi_lds_t;
+__device__ __forceinline__ void sb_rows_issue(__amdgpu_buffer_rsrc_t w, int piece_off, int sb, uint8_t* wl) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(w, (gi_lds_t*)wl, 16, piece_off, sb * 64, 0, 0);
+}
+__device__ __forceinline__ void sb_rows_read(const uint8_t* wl, int n, u32x4 (&w)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) w[q] = *reinterpret_cast<const u32x4*>(wl + 16 * (n + 16 * q));
+}
 
 // Raw buffer loads: a uniform base (the expert's planes, the activations), a
 // loop-invariant lane offset and a uniform superblock offset, so the loop needs no
@@ -63,28 +79,35 @@ struct GiStreams {
   int w_off, s_off, x_off;  // lane byte offsets: row rn's data and d, token row + group g
 };
 
-// Loads of superblock sb of row n (and of the token's activations at the same K).
-__device__ __forceinline__ void gi_issue(const GiStreams& st, int sb, GiBuf& b) {
+// Loads of superblock sb: the weight pieces of both matrices into the wave's LDS
+// buffer wl ([matrix][lane] 16 bytes), d and the token's activations at the same K
+// into registers. GI_LOADS vector-memory instructions in all: the compute waits
+// for a buffer by that count, since the compiler does not track the LDS writes.
+constexpr int GI_LOADS = 12;
+__device__ __forceinline__ void gi_issue(const GiStreams& st, int sb, int piece_off, uint8_t* wl, GiBuf& b) {
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++) {
+  for (int mt = 0; mt < 2; mt++) sb_rows_issue(st.w[mt], piece_off, sb, wl + 1024 * mt);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      b.w[mt][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.w[mt], st.w_off + 16 * i, sb * 64, 0));
-    b.d[mt] = __builtin_amdgcn_raw_buffer_load_b16(st.s[mt], st.s_off, sb * 2, 0);
-  }
+  for (int mt = 0; mt < 2; mt++) b.d[mt] = __builtin_amdgcn_raw_buffer_load_b16(st.s[mt], st.s_off, sb * 2, 0);
 #pragma unroll
   for (int j = 0; j < 8; j++)
     b.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(st.x, st.x_off + 64 * j, sb * 512, 0));
 }
 
-__device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* t, f32x4_t (&acc)[2]) {
+// One superblock from buffer (b, wl), issued before the other buffer's GI_LOADS.
+__device__ __forceinline__ void gi_compute(const GiBuf& b, const uint8_t* wl, int n, int g, const Iq2Lds* t,
+                                           f32x4_t (&acc)[2]) {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GI_LOADS) : "memory");
+  u32x4 w[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) sb_rows_read(wl + 1024 * mt, n, w[mt]);
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const float d8 = half_bits_f32(b.d[mt]) * 0.125f;
     f32x4_t c[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const uint32_t a0 = b.w[mt][j >> 1][2 * (j & 1)], a1 = b.w[mt][j >> 1][2 * (j & 1) + 1];
+      const uint32_t a0 = w[mt][j >> 1][2 * (j & 1)], a1 = w[mt][j >> 1][2 * (j & 1) + 1];
       const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
       const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
       const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
@@ -97,7 +120,7 @@ __device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* 
     }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const uint32_t a1 = b.w[mt][j >> 1][2 * (j & 1) + 1];
+      const uint32_t a1 = w[mt][j >> 1][2 * (j & 1) + 1];
       const float db = d8 * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
 #pragma unroll
       for (int r = 0; r < 4; r++) acc[mt][r] = __builtin_fmaf(c[j][r], db, acc[mt][r]);
@@ -107,12 +130,18 @@ __device__ __forceinline__ void gi_compute(const GiBuf& b, int g, const Iq2Lds* 
 
 __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_gu_iq2(GemvParams P) {
   __shared__ Iq2Lds lds_tab[1];
+  // the two weight buffers of each wave, as two arrays: the compiler then knows
+  // that reading one need not wait for the loads still filling the other
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf0[GI_WAVES][2048];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf1[GI_WAVES][2048];
   iq2_fill_lds(&lds_tab[0], P.grid, threadIdx.x, 64 * GI_WAVES);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
+  uint8_t* const wl0 = &wbuf0[wave][0];
+  uint8_t* const wl1 = &wbuf1[wave][0];
   const int slot = blockIdx.y;
   if (slot >= P.route.n_slots()[0]) return;
   const int e = P.route.slots()[slot];
@@ -147,19 +176,23 @@ __global__ __launch_bounds__(64 * GI_WAVES) __attribute__((amdgpu_waves_per_eu(2
     const int pa = P.route.perm()[pstart + min(m0 + n, M - 1)];
     st.x_off = (pa / P.top_k) * P.cols * 2 + 16 * g;
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    const int poff = st.w_off + 16 * g;
     GiBuf A, B;
-    gi_issue(st, 0, A);
+    gi_issue(st, 0, poff, wl0, A);
     // Two buffers in turn; the prefetch is unconditional (after the last
     // superblock it re-reads it, a cache hit), so no branch separates a prefetch
-    // from the arithmetic after it.
+    // from the arithmetic after it. A buffer's LDS is refilled only after the
+    // compute that read it, whose reads have returned (their values were used).
     for (int sb = 0;; sb += 2) {
-      gi_issue(st, min(sb + 1, nsb - 1), B);
       __builtin_amdgcn_sched_barrier(0);
-      gi_compute(A, g, &lds_tab[0], acc);
+      gi_issue(st, min(sb + 1, nsb - 1), poff, wl1, B);
+      __builtin_amdgcn_sched_barrier(0);
+      gi_compute(A, wl0, n, g, &lds_tab[0], acc);
       if (sb + 1 >= nsb) break;
-      gi_issue(st, min(sb + 2, nsb - 1), A);
       __builtin_amdgcn_sched_barrier(0);
-      gi_compute(B, g, &lds_tab[0], acc);
+      gi_issue(st, min(sb + 2, nsb - 1), poff, wl0, A);
+      __builtin_amdgcn_sched_barrier(0);
+      gi_compute(B, wl1, n, g, &lds_tab[0], acc);
       if (sb + 2 >= nsb) break;
     }
     // The final prefetch is never used: let it land before the registers are reused.
