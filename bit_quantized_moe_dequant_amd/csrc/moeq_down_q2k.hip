@@ -301,7 +301,7 @@ __global__ __launch_bounds__(64 * QD_KPARTS * QD_SLOTS) QD_ATTR void k_down1_q2k
 constexpr int QG_WAVES = 4;
 constexpr int QG_ROWS = 16 * QG_WAVES;
 constexpr int QG_SB = 8;  // superblocks along K (K <= 2048)
-constexpr int QG_WLOADS = 3 * QG_SB;  // a wave's weight and record loads, fewest after merging
+constexpr int QG_WLOADS = QG_SB;  // a wave's weight loads (the records go through LDS)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -386,6 +386,11 @@ struct QgStage {
 template <int NG>
 __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const uint8_t* __restrict__ dq,
                                                             const uint8_t* __restrict__ dsc) {
+  // Each wave's 16 rows of scale records (20 bytes per row and superblock), copied
+  // in once: read from memory by every lane, each record dword came from 16 rows'
+  // lines per instruction, two instructions per superblock against one for the
+  // weights (IQ2_XXS + Q2_K layer at T = 64: 537 against 517 us).
+  __shared__ uint32_t srec[QG_WAVES][16 * QG_SB * 5];
   constexpr int CH = 4 * NG;  // pairs per pass
   __shared__ QgStage<NG> st;
   const int lane = threadIdx.x & 63;
@@ -413,8 +418,14 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
   const int rn = min(n0 + n, P.rows - 1);
   // row rn of the expert: its data and its scale records
   const uint8_t* wrow = P.w[0].data + (size_t)e * P.w[0].estride + (size_t)rn * nsb * 64 + 16 * g;
-  const uint32_t* srow =
-      reinterpret_cast<const uint32_t*>(P.w[0].scales + (size_t)e * P.w[0].sestride + (size_t)rn * nsb * 20);
+  // the records of rows rb .. rb + nrow - 1 (the wave's rows, or the expert's last
+  // row for a wave past the end), contiguous in the scale plane
+  const int rb = min(n0, P.rows - 1), nrow = max(1, min(16, P.rows - rb));
+  const int nrec = nrow * nsb * 5;  // dwords
+  const __amdgpu_buffer_rsrc_t rec_buf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(P.w[0].scales + (size_t)e * P.w[0].sestride + (size_t)rb * nsb * 20), (short)0,
+      0x7FFFFFFF, 0x00020000);
+  const uint32_t* srow = &srec[wave][(rn - rb) * nsb * 5];
   const int t = lane & 3, ip = (lane >> 2) & 3;  // this lane's A row: digit t of pair 4 G + ip
   int pa[NG], po[NG];
   float rwo[NG];
@@ -459,25 +470,22 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
     }
   };
 
-  // The first pass's stage goes out before the weights, so that the wait for it
-  // below leaves the weight loads in flight and each superblock waits only for its
-  // own. All of K for row rn: chunk g of each superblock, and the scale record dwords
-  // of chunk g's sub-blocks (planes 0, 1: dword 2 (g >> 1); planes 2, 3: the next) and
-  // d | dmin (superblocks past the end re-read the last and are not used): QG_WLOADS
-  // loads, none of which can be merged (the record dwords are at lane-dependent
-  // offsets but for the first two, which at most become one).
+  // The first pass's stage and the records go out before the weights, so that the
+  // wait for them below leaves the weight loads in flight and each superblock waits
+  // only for its own. All of K for row rn: chunk g of each superblock (superblocks
+  // past the end re-read the last and are not used), QG_WLOADS loads. Lane (n, g)
+  // later takes from its row's records the dwords of chunk g's sub-blocks (planes
+  // 0, 1: dword 2 (g >> 1); planes 2, 3: the next) and d | dmin.
   stage_issue(0);
   __builtin_amdgcn_sched_barrier(0);
+  // the wave's records straight into LDS, one dword per lane per load
+  for (int k = 0; 64 * k < nrec; k++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rec_buf, (lds_void_t*)&srec[wave][64 * k], 4,
+                                             4 * min(64 * k + lane, nrec - 1), 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 q[QG_SB];
-  uint32_t rlo[QG_SB], rhi[QG_SB], rdd[QG_SB];
 #pragma unroll
-  for (int i = 0; i < QG_SB; i++) {
-    const int sbc = min(i, nsb - 1);
-    q[i] = ld16(wrow + sbc * 64);
-    rlo[i] = srow[5 * sbc + 2 * (g >> 1)];
-    rhi[i] = srow[5 * sbc + 2 * (g >> 1) + 1];
-    rdd[i] = srow[5 * sbc + 4];
-  }
+  for (int i = 0; i < QG_SB; i++) q[i] = ld16(wrow + min(i, nsb - 1) * 64);
   __builtin_amdgcn_sched_barrier(0);
 
   // One pass over the stage (pairs c0 .. c0 + CH - 1). The empty asm at the top of
@@ -493,13 +501,14 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
 #pragma unroll
     for (int i = 0; i < QG_SB; i++) {
       if (i < nsb) {
-        asm volatile("" : "+v"(q[i]), "+v"(rlo[i]), "+v"(rhi[i]), "+v"(rdd[i]));
+        uint32_t rlo_i = srow[5 * i + 2 * (g >> 1)], rhi_i = srow[5 * i + 2 * (g >> 1) + 1], rdd_i = srow[5 * i + 4];
+        asm volatile("" : "+v"(q[i]), "+v"(rlo_i), "+v"(rhi_i), "+v"(rdd_i));
         const int sa = (int)st.sc[i][lane];
         f32x4_t cr[NG], cm[NG];
 #pragma unroll
         for (int pp = 0; pp < 2; pp++) {
           i32x8_t B1, B2, B3;
-          qg_operands(q[i], (pp ? rhi[i] : rlo[i]) >> (8 * (g & 1)), pp, B1, B2, B3);
+          qg_operands(q[i], (pp ? rhi_i : rlo_i) >> (8 * (g & 1)), pp, B1, B2, B3);
 #pragma unroll
           for (int G = 0; G < NG; G++) {
             if (G < ng) {
@@ -513,7 +522,7 @@ __global__ __launch_bounds__(64 * QG_WAVES) void k_dn_q2k_g(GemvParams P, const 
             }
           }
         }
-        const float d = half_bits_f32(rdd[i]), dmin = half_bits_f32(rdd[i] >> 16);
+        const float d = half_bits_f32(rdd_i), dmin = half_bits_f32(rdd_i >> 16);
 #pragma unroll
         for (int G = 0; G < NG; G++)
           if (G < ng)
