@@ -78,6 +78,7 @@ __global__ __launch_bounds__(GU_NT) void k_gu_fp4_g(GemvParams P) {
   constexpr int TILE = NV ? GU_TILE / 2 : GU_TILE;
   __shared__ GuStage st;
   __shared__ float red[GU_WAVES][2][GU_TILE][16];
+  __shared__ __attribute__((aligned(16))) uint8_t scs[GU_WAVES][2][1024];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -151,18 +152,40 @@ __global__ __launch_bounds__(GU_NT) void k_gu_fp4_g(GemvParams P) {
   u32x4 q[2][GU_STEPS];
   u32x4 sbv4[2][NSB];
   const float s2g = NV ? P.w[0].scale2[e] : 1.f, s2u = NV ? P.w[1].scale2[e] : 1.f;
+  static_assert(16 * NSB <= 64, "a wave's scale runs fit one copy instruction per matrix");
+  {
+    // The wave's 16 rows' scale runs copied into LDS once: lane l takes run l % NSB
+    // of row l / NSB (row r at bytes 16 NSB r of the wave's buffer). Loaded by each
+    // lane instead, every run came from 16 rows' lines per instruction, four lanes
+    // per row asking for the same bytes (NVFP4 + Q2_K at T = 64: 639 against 594 us,
+    // the MXFP4 layer 741 against 725 us).
+    const int pr = min(lane / NSB, 15), pc = lane % NSB;
+    const int r = min(n0 + pr, P.rows - 1);
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+      const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(P.w[mt].scales + (size_t)e * P.w[mt].sestride), (short)0, 0x7FFFFFFF, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          sr, (__attribute__((address_space(3))) void*)&scs[wave][mt][0], 16,
+          r * (K / 128 * SPB) + min(SPB * s0 + 16 * pc, SPB * nsteps - 16), 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the copies before every weight load
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const uint8_t* wd = P.w[mt].data + (size_t)e * P.w[mt].estride + (size_t)rn * (K / 2);
-    const uint8_t* ws = P.w[mt].scales + (size_t)e * P.w[mt].sestride + (size_t)rn * (K / 128 * SPB);
-#pragma unroll
-    for (int j = 0; j < NSB; j++) sbv4[mt][j] = ld16(ws + (size_t)min(SPB * s0 + 16 * j, SPB * nsteps - 16));
 #pragma unroll
     for (int i = 0; i < GU_STEPS; i++)
       q[mt][i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
   }
   __builtin_amdgcn_sched_barrier(0);
   stage_convert(0);
+  // the copies landed: only the weight loads issued after them may still be in flight
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * GU_STEPS) : "memory");
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int j = 0; j < NSB; j++) sbv4[mt][j] = *reinterpret_cast<const u32x4*>(&scs[wave][mt][16 * (NSB * n + j)]);
 
   const int pj = n >> 1, term = n & 1;  // this lane's A row: pair pj of the tile, its term
   for (int m0 = 0; m0 < M; m0 += TILE) {

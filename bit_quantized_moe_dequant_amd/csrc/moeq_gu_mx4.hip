@@ -110,6 +110,8 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
   constexpr bool NV = FMT == FMT_NVFP4;
   __shared__ MxStage st;
   __shared__ float red[MX_WAVES][2][16];
+  // NVFP4: the wave's scale runs, copied in once (see below)
+  __shared__ __attribute__((aligned(16))) uint8_t scs[NV ? MX_WAVES : 1][2][NV ? 1024 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -153,11 +155,32 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
   // bytes). Every valid run lies inside the row (my_steps is a multiple of 4).
   constexpr int NSB = MX_STEPS * SPB / 16;
   u32x4 sbv4[2][NSB];
+  if constexpr (NV) {
+    // NVFP4 (twice the scale bytes): the wave's 16 rows' runs are copied into LDS
+    // once, lane l taking run l % NSB of row l / NSB (row r at bytes 16 NSB r), and
+    // read back after the conversion of x. Loaded by each lane, every run came from
+    // 16 rows' lines per instruction, four lanes per row asking for the same bytes
+    // (bs=1 NVFP4 + Q2_K layer 22.41 against 21.82 us). For MXFP4 the copy and its
+    // wait cost more than they save (19.53 against 20.00 us per layer).
+    static_assert(16 * NSB <= 64, "a wave's scale runs fit one copy instruction per matrix");
+    const int pr = min(lane / NSB, 15), pc = lane % NSB;
+    const int r = min(n0 + pr, P.rows - 1);
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++) {
+    for (int mt = 0; mt < 2; mt++) {
+      const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(P.w[mt].scales + (size_t)ec * P.w[mt].sestride), (short)0, 0x7FFFFFFF, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          sr, (__attribute__((address_space(3))) void*)&scs[wave][mt][0], 16,
+          r * (K / 128 * SPB) + min(SPB * s0 + 16 * pc, SPB * nsteps - 16), 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the copies before every weight load
+  } else {
 #pragma unroll
-    for (int j = 0; j < NSB; j++)
-      sbv4[mt][j] = ld16(ws[mt] + (size_t)min(SPB * s0 + 16 * j, SPB * nsteps - 16));
+    for (int mt = 0; mt < 2; mt++) {
+#pragma unroll
+      for (int j = 0; j < NSB; j++)
+        sbv4[mt][j] = ld16(ws[mt] + (size_t)min(SPB * s0 + 16 * j, SPB * nsteps - 16));
+    }
   }
   // Step i's chunk of row rn (steps past the wave's last re-read that one).
   auto load_step = [&](int i) {
@@ -216,6 +239,15 @@ __global__ __launch_bounds__(64 * MX_WAVES) void k_gu1_fp4(GemvParams P) {
     }
   }
   __syncthreads();
+  if constexpr (NV) {
+    // the copies landed: only the DEPTH steps' weight loads issued after them may
+    // still be in flight (the compiler does not track the copies' LDS writes)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DEPTH) : "memory");
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int j = 0; j < NSB; j++) sbv4[mt][j] = *reinterpret_cast<const u32x4*>(&scs[wave][mt][16 * (NSB * n + j)]);
+  }
 
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   float accn[2] = {0.f, 0.f};  // NVFP4: this lane's scaled block sums
