@@ -420,6 +420,9 @@ int run_prefill_down(const moeq_layer* L, const uint8_t* hq, const uint8_t* hs, 
   memset(&p, 0, sizeof(p));
   p.w[0] = ref_of(L->down);
   p.w[1] = p.w[0];
+  // the kernel's second weight tile of each wave: the same matrix 128 rows on
+  p.w[1].data += (size_t)128 * (L->inter / 2);
+  p.w[1].scales += (size_t)128 * (L->inter / 32);
   p.rows = L->hidden;
   p.cols = L->inter;
   p.n_experts = L->n_experts;

@@ -25,8 +25,11 @@
 // route kernel lists the 64-pair chunks of every expert. Each wave owns 32 rows:
 // for gate/up it streams the gate and the up rows of the same 32 features, which
 // share every A fragment it reads (half the LDS reads per matrix instruction, and
-// SwiGLU needs no exchange); for down one 32-row tile. Four waves make a
-// work-group, two (gate/up) or three (down) of which share a compute unit.
+// SwiGLU needs no exchange); for down two 32-row tiles of the down matrix, 128
+// rows apart, which share the A fragments the same way (with one tile per wave the
+// A tile was as many bytes as the weights, and the layer took 911-916 against
+// 891 us at T = 2048). Four waves make a work-group, two of which share a compute
+// unit.
 // K advances in chunks of 256 (eight 32-blocks): the chunk's A tile (64 token
 // rows x 256 bytes, gathered through the routing permutation) is staged once in
 // LDS, double-buffered, and shared by the group's waves; the weights go straight
@@ -51,17 +54,26 @@ typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int PF_KC = 256;                 // K per chunk
-// Waves per work-group: 4. Gate/up waves need about 250 registers, so two groups
-// share a compute unit; down waves get up to 168, three groups to a unit (at 128
-// the compiler spills loop-invariant addresses, and every reload waits for the
-// whole load queue). Several independent groups per unit let one's prologue and
-// epilogue overlap the others' weight streams.
+// Waves per work-group: 4. Waves with two weight tiles need about 250 registers,
+// so two groups share a compute unit; a one-tile down wave gets up to 168, three
+// groups to a unit (at 128 the compiler spills loop-invariant addresses, and every
+// reload waits for the whole load queue). Several independent groups per unit let
+// one's prologue and epilogue overlap the others' weight streams.
 __host__ __device__ constexpr int pf_waves(bool) { return 4; }
-__host__ __device__ constexpr int pf_waves_per_simd(bool gate_up) { return gate_up ? 2 : 3; }
+#ifndef MOEQ_PF_DN_TILES
+#define MOEQ_PF_DN_TILES 2
+#endif
+// Weight tiles per wave: gate/up two (the gate and the up rows of the same 32
+// features), down MOEQ_PF_DN_TILES (32-row tiles of the down matrix 128 rows apart).
+__host__ __device__ constexpr int pf_weight_tiles(bool gate_up) { return gate_up ? 2 : MOEQ_PF_DN_TILES; }
+__host__ __device__ constexpr int pf_waves_per_simd(bool gate_up) { return pf_weight_tiles(gate_up) == 2 ? 2 : 3; }
 constexpr int PF_STRIDE = PF_KC + 16;      // LDS row of the A tile, padded by 16 bytes
 
-// weight rows per work-group: 32 per wave (gate/up: 32 features, gate and up rows)
+// weight rows per tile set: 32 per wave (gate/up: 32 features, gate and up rows)
 __host__ __device__ constexpr int pf_rows(bool gate_up) { return 32 * pf_waves(gate_up); }
+// output columns a work-group covers: gate/up one tile set (its tiles are the two
+// matrices), down one per weight tile (tile s is rows 128 s + [0, 128))
+__host__ __device__ constexpr int pf_span(bool gate_up) { return gate_up ? pf_rows(true) : pf_rows(false) * MOEQ_PF_DN_TILES; }
 
 __device__ __forceinline__ v16f mfma_fp8_fp4(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0, sa, 0,
@@ -121,7 +133,6 @@ struct BChunk {
 // 36 bytes (nine words), so a 32-lane read of one word column is conflict-free.
 constexpr int PF_SG = 4;
 constexpr int PF_SROW = 8 * PF_SG + 4;
-__host__ __device__ constexpr int pf_weight_tiles(bool gate_up) { return gate_up ? 2 : 1; }
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((
@@ -148,14 +159,15 @@ __global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((
   const int e = P.route.chunk_e()[q];
   const int pstart = P.route.offsets()[e] + P.route.chunk_m0()[q];
   const int M = min(PREFILL_MC, P.route.offsets()[e + 1] - pstart);
-  const int nbase = blockIdx.x * ROWS;
+  constexpr int SPAN = pf_span(GATE_UP);
+  const int nbase = blockIdx.x * SPAN;
 
   if (tid < PREFILL_MC) pair_lds[tid] = tid < M ? P.route.perm()[pstart + tid] : 0;
   __syncthreads();
 
   if (e >= P.n_experts) {  // bucket of out-of-range ids: outputs are zero
-    for (int i = tid; i < M * ROWS; i += PF_THREADS) {
-      const int m = i / ROWS, col = nbase + i % ROWS;
+    for (int i = tid; i < M * SPAN; i += PF_THREADS) {
+      const int m = i / SPAN, col = nbase + i % SPAN;
       const size_t pair = (size_t)pair_lds[m];
       if (GATE_UP) {
         P.hq[pair * P.rows + col] = 0;
@@ -489,17 +501,19 @@ __global__ __launch_bounds__(64 * pf_waves(GATE_UP)) __attribute__((
         w[r] = rw_lds[m];
       }
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        if (32 * t + (r & 3) + 8 * (r >> 2) + 4 * g < M)
-          P.partial[(size_t)pr[r] * P.rows + n0 + n] = acc[0][t][r] * w[r];
-      }
+      for (int s = 0; s < NS; s++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          if (32 * t + (r & 3) + 8 * (r >> 2) + 4 * g < M)
+            P.partial[(size_t)pr[r] * P.rows + n0 + ROWS * s + n] = acc[s][t][r] * w[r];
+        }
     }
   }
 }
 
 hipError_t launch_prefill(bool gate_up, const PrefillParams& p, int /*n_slots*/, hipStream_t s) {
   // rows and cols are multiples of 256 (checked by the caller)
-  dim3 g((unsigned)(p.rows / pf_rows(gate_up)), (unsigned)RouteView::max_chunks(p.route.E, p.route.P)),
+  dim3 g((unsigned)(p.rows / pf_span(gate_up)), (unsigned)RouteView::max_chunks(p.route.E, p.route.P)),
       b((unsigned)(64 * pf_waves(gate_up)));
   if (gate_up) hipLaunchKernelGGL(k_prefill<true>, g, b, 0, s, p);
   else hipLaunchKernelGGL(k_prefill<false>, g, b, 0, s, p);
