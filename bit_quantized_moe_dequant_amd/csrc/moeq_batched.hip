@@ -8,9 +8,11 @@
 //
 // The tokens are operand A as E4M3 terms with e8m0 scales per 32, their rows
 // carrying (pair, term) couples:
-//   * gate/up: x (bf16) as two terms; rows 2j, 2j + 1 = pair j of a tile of eight
+//   * gate/up: x (bf16) as two terms; rows 2j, 2j + 1 = pair j of a staged tile
+//     (up to eight per instruction; two staged, see MOEQ_GU_TILE_MX)
 //     (the split is exact to 2^-21.8 of each 32-block's maximum);
-//   * down: h (fp32) as three terms; rows 3j .. 3j + 2 = pair j of a tile of five
+//   * down: h (fp32) as three terms; rows 3j .. 3j + 2 = pair j of a staged tile
+//     (up to five per instruction; two staged, see MOEQ_DN_TILE)
 //     (about 12 significant bits of h).
 // A pair is a (token, slot) of the routing; the route table (the counting sort of
 // the pairs by expert) gives each work-group its expert and the expert's pairs.
@@ -54,18 +56,38 @@ constexpr int GB_STEPS = 8;
 constexpr int GU_WAVES = MOEQ_GU_G_WAVES;  // gate/up waves; their K steps cover K <= 4096
 constexpr int GU_NT = 64 * GU_WAVES;
 constexpr int GU_STEPS = 32 / GU_WAVES;
-constexpr int GU_TILE = 8;           // gate/up pairs per instruction (2 terms each)
+// Gate/up pairs staged per tile. MXFP4: two (an instruction's 16 A rows could take
+// eight pairs of two terms, but at the loads this path serves most experts have one
+// or two pairs, and the smaller stage fits three work-groups per CU instead of two:
+// the MXFP4 layer at T = 64 / 96 took 725 / 882 us with eight-pair tiles, 704 / 862
+// with four, 645 / 802 with two). NVFP4 (one pair per instruction): four (NVFP4 +
+// Q2_K at T = 64 / 256: 586 / 1490 us; 578 / 1512 with two, 606 / 1571 with one).
+#ifndef MOEQ_GU_TILE_MX
+#define MOEQ_GU_TILE_MX 2
+#endif
+#ifndef MOEQ_GU_TILE_NV
+#define MOEQ_GU_TILE_NV 4
+#endif
 constexpr int GU_KMAX = 4096;
-constexpr int DN_TILE = 5;           // down pairs per instruction (3 terms each)
+// Down pairs per staged tile (three terms each; an instruction's A rows hold at most
+// five): two, so that the h staging registers allow four waves per SIMD (110 VGPRs,
+// 17 KB of LDS). The MXFP4 layer at T = 48 / 64 / 96 took 545 / 645 / 803 us with
+// five-pair tiles, 543 / 649 / 824 with three, 511 / 614 / 781 with two.
+#ifndef MOEQ_DN_TILE
+#define MOEQ_DN_TILE 2
+#endif
+constexpr int DN_TILE = MOEQ_DN_TILE;
+static_assert(DN_TILE >= 1 && DN_TILE <= 5, "an instruction's A rows hold at most five pairs");
 constexpr int DN_KMAX = 2048;
 
 // Wave w takes K steps [w spw, (w + 1) spw), spw a multiple of 4 (16-byte runs of
 // scale bytes stay inside the row).
 __device__ __forceinline__ int steps_per_wave(int nsteps, int waves) { return 4 * ((nsteps + 4 * waves - 1) / (4 * waves)); }
 
+template <int TILE>
 struct GuStage {
-  uint8_t code[2][GU_TILE * GU_KMAX];
-  uint8_t sc[2][GU_TILE * GU_KMAX / 32];
+  uint8_t code[2][TILE * GU_KMAX];
+  uint8_t sc[2][TILE * GU_KMAX / 32];
 };
 
 template <int FMT>
@@ -73,11 +95,12 @@ __global__ __launch_bounds__(GU_NT) void k_gu_fp4_g(GemvParams P) {
   constexpr bool NV = FMT == FMT_NVFP4;
   constexpr int SPB = NV ? 8 : 4;            // scale bytes per row and 128-wide step
   constexpr int NSB = GU_STEPS * SPB / 16;   // 16-byte scale runs per wave and row
-  // pairs per staged tile (NVFP4: one pair per instruction; a tile of four keeps
-  // its staging registers small enough for two waves per SIMD)
-  constexpr int TILE = NV ? GU_TILE / 2 : GU_TILE;
-  __shared__ GuStage st;
-  __shared__ float red[GU_WAVES][2][GU_TILE][16];
+  constexpr int TILE = NV ? MOEQ_GU_TILE_NV : MOEQ_GU_TILE_MX;  // pairs per staged tile
+  static_assert(TILE >= 1 && TILE <= 8, "an instruction's A rows hold at most eight pairs");
+  __shared__ GuStage<TILE> st;
+  // partial sums per pair of one instruction: its 16 A rows hold up to eight pairs
+  // (lane group g writes pairs 2g and 2g + 1 whatever the tile)
+  __shared__ float red[GU_WAVES][2][8][16];
   __shared__ __attribute__((aligned(16))) uint8_t scs[GU_WAVES][2][1024];
 
   const int lane = threadIdx.x & 63;

@@ -1,8 +1,8 @@
 """Batched MXFP4 and NVFP4 decode (T > 1) on the block-scaled matrix instruction
-against the CPU oracle. Up to 32 tokens (16 for the NVFP4 gate/up) the
+against the CPU oracle. Up to 24 tokens (16 for the NVFP4 gate/up) the
 single-token kernels run over every (token, slot) pair; beyond, the grouped
-kernels take each routed expert's pairs in tiles of eight (MXFP4 gate/up), four
-(NVFP4 gate/up, one pair per instruction) and five (MXFP4 down). Cases: experts
+kernels take each routed expert's pairs in staged tiles of two (MXFP4 gate/up and
+down) and four (NVFP4 gate/up, one pair per instruction). Cases: experts
 with several tiles of pairs, K of 1024 and 4096 (one and eight steps per wave),
 out-of-range ids on both paths, and the full DeepSeek-V4-Flash-shaped layers at
 16 and 64 tokens (co-scheduled decode sessions)."""
@@ -32,11 +32,13 @@ def x_tensor(bits):
     return cuda(bits.view(np.int16)).view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("T,E,K", [(2, 8, 6), (5, 8, 6), (40, 8, 6), (9, 3, 2), (17, 2, 1), (33, 2, 1), (32, 8, 6)])
+@pytest.mark.parametrize("T,E,K", [(2, 8, 6), (5, 8, 6), (40, 8, 6), (9, 3, 2), (17, 2, 1), (33, 2, 1), (24, 8, 6),
+                                   (25, 8, 6), (32, 8, 6)])
 def test_batched_mxfp4_tiles(T, E, K):
-    """T = 40 over 8 experts gives about 30 pairs per expert: four gate/up tiles and
-    six down tiles, the last partial; T = 33, one slot, two experts: gate/up tiles of
-    8 and a last one of 1 or 2; T = 32 is the largest batch of the direct path."""
+    """T = 40 over 8 experts gives about 30 pairs per expert: fifteen two-pair
+    tiles each for gate/up and down; T = 33, one slot, two experts: an odd expert
+    ends on a one-pair tile; T = 24 is the largest batch of the direct path and
+    T = 25 the smallest of the grouped one."""
     say("batched mxfp4", T, E, K)
     spec = workloads.LayerSpec(1024, 512, E, K, mq.FMT_MXFP4, mq.FMT_MXFP4, seed=6100 + T + E)
     layer = workloads.build_layer(mq, spec)
