@@ -101,30 +101,47 @@ __device__ __forceinline__ void gi_compute(const GiBuf& b, const uint8_t* wl, in
   u32x4 w[2][4];
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) sb_rows_read(wl + 1024 * mt, n, w[mt]);
+  // operand B of sub-block j of matrix mt: the codebook entry with the signs applied
+  auto operand = [&](int mt, int j) {
+    const uint32_t a0 = w[mt][j >> 1][2 * (j & 1)], a1 = w[mt][j >> 1][2 * (j & 1) + 1];
+    const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
+    const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
+    const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
+    const u32x4 m = t->sgn[code];
+    // sign bits of the codebook words are clear, so OR applies the signs
+    return u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
+  };
+  auto product = [&](int mt, int j) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.x[j]),
+                                                   __builtin_bit_cast(bf16x8_t, operand(mt, j)),
+                                                   f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  };
+  float d8[2];
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++) {
-    const float d8 = half_bits_f32(b.d[mt]) * 0.125f;
-    f32x4_t c[8];
+  for (int mt = 0; mt < 2; mt++) d8[mt] = half_bits_f32(b.d[mt]) * 0.125f;
+  auto scale_add = [&](int mt, int j, const f32x4_t& c) {
+    const uint32_t a1 = w[mt][j >> 1][2 * (j & 1) + 1];
+    const float db = d8[mt] * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const uint32_t a0 = w[mt][j >> 1][2 * (j & 1)], a1 = w[mt][j >> 1][2 * (j & 1) + 1];
-      const uint32_t gi = (a0 >> (8 * g)) & 0xFFu;
-      const uint32_t code = (a1 >> (7 * g)) & 0x7Fu;
-      const u32x4 gw = *reinterpret_cast<const u32x4*>(&t->grid[gi * 4]);
-      const u32x4 m = t->sgn[code];
-      // sign bits of the codebook words are clear, so OR applies the signs
-      const u32x4 wv = u32x4{gw[0] | m[0], gw[1] | m[1], gw[2] | m[2], gw[3] | m[3]};
-      c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.x[j]),
-                                                     __builtin_bit_cast(bf16x8_t, wv), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0,
-                                                     0, 0);
+    for (int r = 0; r < 4; r++) acc[mt][r] = __builtin_fmaf(c[r], db, acc[mt][r]);
+  };
+  // Two sub-blocks in flight: the products of sub-block j are issued before the
+  // scaled sums of sub-block j - 1, so only two sub-blocks' results are live (174
+  // -> 152 VGPRs against all eight products of a matrix first; IQ2_XXS + Q2_K at
+  // T = 64 491.5-493.5 -> 486-488 us). Each accumulator still adds its sub-blocks
+  // in order.
+  f32x4_t c[2][2];
+#pragma unroll
+  for (int j = 0; j <= 8; j++) {
+    if (j < 8) {
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) c[j & 1][mt] = product(mt, j);
     }
+    if (j > 0) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const uint32_t a1 = w[mt][j >> 1][2 * (j & 1) + 1];
-      const float db = d8 * (float)(2u * (a1 >> 28) + 1u);  // exact: 11 x 5 bits
-#pragma unroll
-      for (int r = 0; r < 4; r++) acc[mt][r] = __builtin_fmaf(c[j][r], db, acc[mt][r]);
+      for (int mt = 0; mt < 2; mt++) scale_add(mt, j - 1, c[(j - 1) & 1][mt]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
