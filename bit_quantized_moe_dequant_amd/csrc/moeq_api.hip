@@ -261,10 +261,11 @@ bool scales16(const moeq_weight& w) {
 // at T = 2 / 4 / 8 / 16 / 64: 46.3 / 87.3 / 160.0 / 294.6 / 1024 us direct against
 // 58.4 / 89.3 / 149.8 / 255.3 / 702 us with the grouped FP8 down). The routing kernel
 // runs only when a projection takes the grouped path.
-// (MXFP4 layer at T = 16 / 24 / 32: 204 / 300 / 397 us direct against 203 / 309 /
-// 384 us grouped, with the grouped kernels' two-pair tiles.)
+// (MXFP4 layer at T = 8 / 12 / 16 / 24 / 32: 107.7 / 155.5 / 203 / 299 / 397 us
+// direct against 111 / 151.5 / 188 / 252.5 / 309.6 us grouped, with the grouped
+// kernels' two-pair tiles and row-split down.)
 #ifndef MOEQ_FP4_DIRECT_MAX_T
-#define MOEQ_FP4_DIRECT_MAX_T 24
+#define MOEQ_FP4_DIRECT_MAX_T 8
 #endif
 #ifndef MOEQ_NV4_DIRECT_MAX_T
 #define MOEQ_NV4_DIRECT_MAX_T 16

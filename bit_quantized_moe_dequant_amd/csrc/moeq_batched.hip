@@ -50,6 +50,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int GB_WAVES = 4;         // down: four waves of up to eight K steps (K <= 2048 uses four)
 constexpr int GB_NT = 64 * GB_WAVES;
 constexpr int GB_STEPS = 8;
+#ifndef MOEQ_DN_ROWSPLIT
+#define MOEQ_DN_ROWSPLIT 1
+#endif
+// Down work split: 1 = each wave takes its own 16 weight rows over all of K (64 rows
+// per work-group); 0 = the four waves take quarters of K of the same 16 rows.
+constexpr bool DN_ROWSPLIT = MOEQ_DN_ROWSPLIT;
+constexpr int DN_ROWS = DN_ROWSPLIT ? 16 * GB_WAVES : 16;  // weight rows per work-group
 #ifndef MOEQ_GU_G_WAVES
 #define MOEQ_GU_G_WAVES 4
 #endif
@@ -336,22 +343,23 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
   const int e = P.route.slots()[slot];
   const int pstart = P.route.offsets()[e];
   const int M = P.route.offsets()[e + 1] - pstart;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * DN_ROWS;
   if (e >= P.n_experts) {  // out-of-range ids contribute nothing
-    for (int i = threadIdx.x; i < M * 16; i += GB_NT) {
-      const int r = n0 + (i & 15);
-      if (r < P.rows) P.out[(size_t)P.route.perm()[pstart + (i >> 4)] * P.rows + r] = 0.f;
+    for (int i = threadIdx.x; i < M * DN_ROWS; i += GB_NT) {
+      const int r = n0 + (i % DN_ROWS);
+      if (r < P.rows) P.out[(size_t)P.route.perm()[pstart + i / DN_ROWS] * P.rows + r] = 0.f;
     }
     return;
   }
   const int K = P.cols;
   const int nsteps = K / 128;
   const int cpt = K / 16;
-  const int spw = steps_per_wave(nsteps, GB_WAVES);
-  const int s0 = wave * spw;
+  constexpr int DSTEPS = DN_ROWSPLIT ? DN_KMAX / 128 : GB_STEPS;  // K steps per wave, at most
+  const int spw = DN_ROWSPLIT ? nsteps : steps_per_wave(nsteps, GB_WAVES);
+  const int s0 = DN_ROWSPLIT ? 0 : wave * spw;
   const int my = max(0, min(spw, nsteps - s0));
   const int n = lane & 15, g = lane >> 4;
-  const int rn = min(n0 + n, P.rows - 1);
+  const int rn = min(n0 + (DN_ROWSPLIT ? 16 * wave : 0) + n, P.rows - 1);
   constexpr int XC = (DN_TILE * DN_KMAX / 16 + GB_NT - 1) / GB_NT;
 
   u32x4 hv[XC][4];
@@ -394,15 +402,15 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
 
   stage_load(0);
   __builtin_amdgcn_sched_barrier(0);
-  u32x4 q[GB_STEPS];
-  u32x4 sbv4[GB_STEPS / 4];
+  u32x4 q[DSTEPS];
+  u32x4 sbv4[DSTEPS / 4];
   {
     const uint8_t* wd = P.w[0].data + (size_t)e * P.w[0].estride + (size_t)rn * (K / 2);
     const uint8_t* ws = P.w[0].scales + (size_t)e * P.w[0].sestride + (size_t)rn * (K / 32);
 #pragma unroll
-    for (int j = 0; j < GB_STEPS / 4; j++) sbv4[j] = ld16(ws + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
+    for (int j = 0; j < DSTEPS / 4; j++) sbv4[j] = ld16(ws + (size_t)min(4 * (s0 + 4 * j), 4 * (nsteps - 4)));
 #pragma unroll
-    for (int i = 0; i < GB_STEPS; i++) q[i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
+    for (int i = 0; i < DSTEPS; i++) q[i] = ld16(wd + (size_t)min(s0 + min(i, max(my - 1, 0)), nsteps - 1) * 64 + 16 * g);
   }
   __builtin_amdgcn_sched_barrier(0);
   stage_convert(0);
@@ -418,7 +426,7 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
     __syncthreads();
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < GB_STEPS; i++) {
+    for (int i = 0; i < DSTEPS; i++) {
       if (i < my) {
         const int s = s0 + i;
         u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
@@ -439,13 +447,19 @@ __global__ __launch_bounds__(GB_NT) void k_dn_mx4_g(GemvParams P) {
 #pragma unroll
     for (int r = 0; r < 4; r++) red[wave][4 * g + r][n] = acc[r];
     __syncthreads();
-    if (threadIdx.x < 16 * DN_TILE) {
-      const int j = threadIdx.x >> 4, col = threadIdx.x & 15;
-      const int r = n0 + col;
+    // rows split: wave w's own 16 rows; K split: the waves' quarters of K in order
+    if (threadIdx.x < (DN_ROWSPLIT ? GB_WAVES : 1) * 16 * DN_TILE) {
+      const int wr = DN_ROWSPLIT ? (int)threadIdx.x / (16 * DN_TILE) : 0;
+      const int j = ((int)threadIdx.x % (16 * DN_TILE)) >> 4, col = threadIdx.x & 15;
+      const int r = n0 + 16 * wr + col;
       if (j < tn && r < P.rows) {
         float v = 0.f;
+        if constexpr (DN_ROWSPLIT) {
+          v = (red[wr][3 * j][col] + red[wr][3 * j + 1][col]) + red[wr][3 * j + 2][col];
+        } else {
 #pragma unroll
-        for (int w = 0; w < GB_WAVES; w++) v += (red[w][3 * j][col] + red[w][3 * j + 1][col]) + red[w][3 * j + 2][col];
+          for (int w = 0; w < GB_WAVES; w++) v += (red[w][3 * j][col] + red[w][3 * j + 1][col]) + red[w][3 * j + 2][col];
+        }
         const int pair = P.route.perm()[pstart + m0 + j];
         P.out[(size_t)pair * P.rows + r] = v * P.rw[pair];
       }
@@ -472,7 +486,8 @@ hipError_t launch_gu_fp4_g(int fmt, const GemvParams& p, int n_slots, hipStream_
 
 hipError_t launch_dn_mx4_g(const GemvParams& p, int n_slots, hipStream_t s) {
   if (!dn_mx4_g_fits(p.rows, p.cols)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_dn_mx4_g, dim3((unsigned)((p.rows + 15) / 16), (unsigned)n_slots), dim3(GB_NT), 0, s, p);
+  hipLaunchKernelGGL(k_dn_mx4_g, dim3((unsigned)((p.rows + DN_ROWS - 1) / DN_ROWS), (unsigned)n_slots), dim3(GB_NT), 0, s,
+                     p);
   return hipGetLastError();
 }
 
