@@ -63,17 +63,18 @@ constexpr int DN_ROWS = DN_ROWSPLIT ? 16 * GB_WAVES : 16;  // weight rows per wo
 constexpr int GU_WAVES = MOEQ_GU_G_WAVES;  // gate/up waves; their K steps cover K <= 4096
 constexpr int GU_NT = 64 * GU_WAVES;
 constexpr int GU_STEPS = 32 / GU_WAVES;
-// Gate/up pairs staged per tile. MXFP4: two (an instruction's 16 A rows could take
+// Gate/up pairs staged per tile: two. MXFP4: an instruction's 16 A rows could take
 // eight pairs of two terms, but at the loads this path serves most experts have one
-// or two pairs, and the smaller stage fits three work-groups per CU instead of two:
-// the MXFP4 layer at T = 64 / 96 took 725 / 882 us with eight-pair tiles, 704 / 862
-// with four, 645 / 802 with two). NVFP4 (one pair per instruction): four (NVFP4 +
-// Q2_K at T = 64 / 256: 586 / 1490 us; 578 / 1512 with two, 606 / 1571 with one).
+// or two pairs, and the smaller stage fits three work-groups per CU instead of two
+// (the MXFP4 layer at T = 64 / 96 took 725 / 882 us with eight-pair tiles, 704 / 862
+// with four, 645 / 802 with two). NVFP4 (one pair per instruction): with two the
+// kernel fits 147 VGPRs and three work-groups per CU (NVFP4 + Q2_K at T = 64 / 256:
+// 583 / 1485 us with four-pair tiles, 510 / 1269 with two).
 #ifndef MOEQ_GU_TILE_MX
 #define MOEQ_GU_TILE_MX 2
 #endif
 #ifndef MOEQ_GU_TILE_NV
-#define MOEQ_GU_TILE_NV 4
+#define MOEQ_GU_TILE_NV 2
 #endif
 constexpr int GU_KMAX = 4096;
 // Down pairs per staged tile (three terms each; an instruction's A rows hold at most
@@ -285,7 +286,10 @@ __global__ __launch_bounds__(GU_NT) void k_gu_fp4_g(GemvParams P) {
               const f32x4_t c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   av, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, sa, 0, 127);
               // E4M3 scales of blocks 4 (g & 1) + r of step s for row n: one word
-              const uint32_t sw = sbv4[mt][i >> 1][2 * (i & 1) + (g & 1)];
+              uint32_t sw = sbv4[mt][i >> 1][2 * (i & 1) + (g & 1)];
+              // converted again for each pair: hoisted out of the pair loop, the 64
+              // converted scales took 48 registers (223 against 175 VGPRs)
+              asm volatile("" : "+v"(sw));
               const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
               const f32x2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, true);
               float a = accn[mt];

@@ -2,7 +2,7 @@
 against the CPU oracle. Up to 8 tokens (16 for the NVFP4 gate/up) the
 single-token kernels run over every (token, slot) pair; beyond, the grouped
 kernels take each routed expert's pairs in staged tiles of two (MXFP4 gate/up and
-down) and four (NVFP4 gate/up, one pair per instruction). Cases: experts
+down, and the NVFP4 gate/up, one pair per instruction). Cases: experts
 with several tiles of pairs, K of 1024 and 4096 (one and eight steps per wave),
 out-of-range ids on both paths, and the full DeepSeek-V4-Flash-shaped layers at
 16 and 64 tokens (co-scheduled decode sessions)."""
