@@ -99,7 +99,10 @@ struct GuStage {
 };
 
 template <int FMT>
-__global__ __launch_bounds__(GU_NT) void k_gu_fp4_g(GemvParams P) {
+// A budget of three waves per SIMD (147 VGPRs for both formats, no spills; 155 for
+// MXFP4 unasked): NVFP4 + Q2_K at T = 256 1265 -> 1224 us, T = 64 503 -> 498 us, the
+// MXFP4 layer at T = 64 479.5 -> 476 us. Four waves spill 16-20 VGPRs and lose 25-40%.
+__global__ __launch_bounds__(GU_NT) __attribute__((amdgpu_waves_per_eu(3))) void k_gu_fp4_g(GemvParams P) {
   constexpr bool NV = FMT == FMT_NVFP4;
   constexpr int SPB = NV ? 8 : 4;            // scale bytes per row and 128-wide step
   constexpr int NSB = GU_STEPS * SPB / 16;   // 16-byte scale runs per wave and row
