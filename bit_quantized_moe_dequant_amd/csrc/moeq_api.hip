@@ -271,12 +271,11 @@ bool scales16(const moeq_weight& w) {
 #define MOEQ_NV4_DIRECT_MAX_T 16
 #endif
 // IQ2_XXS gate/up: the dequantize + GEMV over every pair below this load (pairs per
-// touched expert): IQ2_XXS + Q2_K at T = 2 / 8 / 16 / 32 (1.0 / 1.1 / 1.2 / 1.4
-// pairs): 48.2 / 165 / 296 / 555 us against 72.3 / 198 / 344 / 564 us with the
-// token-grouped kernel, whose 16-token tiles are mostly empty there; at T = 48
-// (1.7 pairs) 799 against 758 us.
+// touched expert), i.e. up to 3 tokens over 256 experts: IQ2_XXS + Q2_K at T = 2 /
+// 3 / 4 / 8 / 16 / 32 took 41.7 / 58.0 / 75.1 / 143.5 / 259 / 479 us with the GEMV
+// against 49.2 / 65.3 / 73.0 / 126.5 / 210 / 333 us with the token-grouped kernel.
 #ifndef MOEQ_IQ2_DIRECT_BELOW
-#define MOEQ_IQ2_DIRECT_BELOW 1.5
+#define MOEQ_IQ2_DIRECT_BELOW 1.03
 #endif
 #ifndef MOEQ_Q2K_DIRECT_BELOW
 #define MOEQ_Q2K_DIRECT_BELOW 1.06

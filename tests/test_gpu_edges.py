@@ -209,15 +209,17 @@ def test_iq2_grouped_down_tiles(T, E, K):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T", [3, 8])
-def test_iq2_direct_few_tokens(T):
-    """IQ2_XXS gate/up + Q2_K down for a few tokens over 64 experts (about 1.1 and
-    1.4 pairs per touched expert): both projections run over every (token, slot)
-    pair without routing. One out-of-range id must give zero h and add nothing."""
-    say("iq2 direct", T)
-    spec = workloads.LayerSpec(1024, 512, 64, 6, mq.FMT_IQ2_XXS, mq.FMT_Q2_K, seed=5600 + T)
+@pytest.mark.parametrize("E,T", [(256, 2), (256, 3), (64, 8)])
+def test_iq2_direct_few_tokens(E, T):
+    """IQ2_XXS gate/up + Q2_K down for a few tokens. Over 256 experts at T = 2 and 3
+    (1.01 and 1.02 pairs per touched expert) both projections run over every
+    (token, slot) pair without routing; over 64 experts at T = 8 (1.36 pairs) the
+    gate/up is token-grouped and the Q2_K down grouped on the FP8 instruction. One
+    out-of-range id must give zero h and add nothing."""
+    say("iq2 few tokens", E, T)
+    spec = workloads.LayerSpec(1024, 512, E, 6, mq.FMT_IQ2_XXS, mq.FMT_Q2_K, seed=5600 + T)
     layer = workloads.build_layer(mq, spec)
-    ids, rw = synth.uniform_routing(spec.seed, T, 64, 6)
+    ids, rw = synth.uniform_routing(spec.seed, T, E, 6)
     x = synth.activations_bf16(spec.seed + 1, T, 1024)
     bad = ids.copy()
     bad[T - 1, 4] = -3
@@ -230,6 +232,7 @@ def test_iq2_direct_few_tokens(T):
     xt, it = x_tensor(x), cuda(bad)
     y = mq.expert_forward(layer, xt, it, cuda(rw), ws=ws).cpu().numpy()
     assert mq.check_device_error(ws) & mq.DEVERR_EXPERT_ID
+    mq.route(layer, it, ws=ws)
     h = mq.gate_up(layer, xt, it, ws=ws).cpu().numpy().reshape(T, 6, 512)
     assert np.all(h[T - 1, 4] == 0.0)
     ok = np.ones((T, 6), bool)
