@@ -238,11 +238,11 @@ bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >=
 #endif
 // NVFP4 gate/up off the direct path: on the same token-grouped kernel (one pair per
 // instruction) from this many pairs per touched expert, as grouped GEMVs below it.
-// NVFP4 + Q2_K layers at T = 32 / 64 / 256 (1.4 / 1.9 / 6 pairs): 429 / 652 / 1544 us
-// against 425 / 686 / 1661 us with the GEMVs; at T = 16 the direct path stays ahead
-// (256 against 268 us).
+// Since the grouped kernel fits three work-groups per CU it is ahead at every load
+// (NVFP4 + Q2_K at T = 24 / 32: 266 / 327 us against 317 / 397 us with the GEMVs),
+// so the GEMVs no longer take this path.
 #ifndef MOEQ_NV4_GROUPED_FROM
-#define MOEQ_NV4_GROUPED_FROM 1.5
+#define MOEQ_NV4_GROUPED_FROM 0.0
 #endif
 
 // Scale plane read in 16-byte runs by the matrix-instruction kernels.
@@ -255,8 +255,7 @@ bool scales16(const moeq_weight& w) {
 // expert routed by several tokens is read once per pair). The gate/up takes this
 // path for MXFP4 up to MOEQ_FP4_DIRECT_MAX_T tokens and for NVFP4 up to
 // MOEQ_NV4_DIRECT_MAX_T (the block-scaled matrix-unit kernels; NVFP4 + Q2_K at
-// T = 2 / 8 / 16 / 32: 41.8 / 149 / 264 / 485 us against 49.1 / 160 / 270 / 477 us
-// grouped); the down for MXFP4 up to MOEQ_FP4_DIRECT_MAX_T, for Q2_K below a load
+// T = 8 / 12 / 16: 122 / 170 / 217 us direct against 118 / 159 / 197 us grouped); the down for MXFP4 up to MOEQ_FP4_DIRECT_MAX_T, for Q2_K below a load
 // of MOEQ_Q2K_DIRECT_BELOW pairs per touched expert (0 turns that off; NVFP4 + Q2_K
 // at T = 2 / 4 / 8 / 16 / 64: 46.3 / 87.3 / 160.0 / 294.6 / 1024 us direct against
 // 58.4 / 89.3 / 149.8 / 255.3 / 702 us with the grouped FP8 down). The routing kernel
@@ -268,7 +267,7 @@ bool scales16(const moeq_weight& w) {
 #define MOEQ_FP4_DIRECT_MAX_T 8
 #endif
 #ifndef MOEQ_NV4_DIRECT_MAX_T
-#define MOEQ_NV4_DIRECT_MAX_T 16
+#define MOEQ_NV4_DIRECT_MAX_T 4
 #endif
 // IQ2_XXS gate/up: the dequantize + GEMV over every pair below this load (pairs per
 // touched expert), i.e. up to 3 tokens over 256 experts: IQ2_XXS + Q2_K at T = 2 /

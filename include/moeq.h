@@ -13,7 +13,7 @@
  * MXFP4 and NVFP4 gate/up and MXFP4 down feed the FP4 codes straight into the
  * block-scaled matrix instruction, and the Q2_K down its 2-bit codes as FP8
  * operands of the same instruction; IQ2_XXS and the remaining shapes decode on the
- * VALU (dequantize + GEMV). Up to 8 tokens (16 for NVFP4 gate/up; Q2_K down below
+ * VALU (dequantize + GEMV). Up to 8 tokens (4 for NVFP4 gate/up; Q2_K down below
  * 1.06 pairs per touched expert) these kernels run over every (token, slot) pair
  * with no routing step; beyond, each routed expert is read once per step for all
  * of its tokens (MXFP4, the NVFP4 gate/up and the Q2_K down on the block-scaled

@@ -1,5 +1,5 @@
 """Batched MXFP4 and NVFP4 decode (T > 1) on the block-scaled matrix instruction
-against the CPU oracle. Up to 8 tokens (16 for the NVFP4 gate/up) the
+against the CPU oracle. Up to 8 tokens (4 for the NVFP4 gate/up) the
 single-token kernels run over every (token, slot) pair; beyond, the grouped
 kernels take each routed expert's pairs in staged tiles of two (MXFP4 gate/up and
 down, and the NVFP4 gate/up, one pair per instruction). Cases: experts
@@ -101,13 +101,13 @@ def test_batched_mxfp4_full_layer(T, sample):
 
 
 @pytest.mark.parametrize("H,T,E,K", [(1024, 17, 8, 6), (1024, 40, 8, 6), (1024, 22, 2, 1), (4096, 24, 8, 6),
-                                     (1024, 33, 64, 6), (1024, 20, 256, 6)])
+                                     (1024, 33, 64, 6), (1024, 20, 256, 6), (1024, 4, 8, 6), (1024, 5, 8, 6)])
 def test_batched_nvfp4_gate_up_tiles(H, T, E, K):
-    """NVFP4 gate/up on the grouped kernel (from 17 tokens and 1.5 pairs per touched
-    expert): 12.75 and 30 pairs per expert (tiles of four, the last partial), two
-    experts of 11 pairs, hidden 4096 (eight K steps per wave), about 3.2 pairs per
-    expert over 64 experts; and the grouped GEMV below 1.5 pairs (T = 20 over 256
-    experts)."""
+    """NVFP4 gate/up on the grouped kernel (from 5 tokens): 12.75 and 30 pairs per
+    expert (two-pair tiles, the last partial), two experts of 11 pairs, hidden 4096
+    (eight K steps per wave), about 3.2 pairs per expert over 64 experts, 1.2 over
+    256 experts (T = 20), and T = 5, the smallest grouped batch; T = 4 is the largest
+    batch of the direct path."""
     say("batched nvfp4", H, T, E, K)
     spec = workloads.LayerSpec(H, 512, E, K, mq.FMT_NVFP4, mq.FMT_MXFP4, seed=6300 + T + E + H)
     layer = workloads.build_layer(mq, spec)
@@ -146,7 +146,7 @@ def test_batched_nvfp4_out_of_range_id():
     assert rel_err(y, ref_y) < TOL
 
 
-@pytest.mark.parametrize("T,sample", [(64, [0, 31, 63])])
+@pytest.mark.parametrize("T,sample", [(16, [0, 5, 15]), (64, [0, 31, 63])])
 def test_batched_nvfp4_q2k_full_layer(T, sample):
     """The NVFP4 + Q2_K layer of the DeepSeek-V4-Flash shape at 64 co-scheduled
     tokens: grouped NVFP4 gate/up and grouped Q2_K down."""
