@@ -212,10 +212,12 @@ double pairs_per_expert(const moeq_layer* L, int T) {
 bool grouped_wide(const moeq_layer* L, int T) { return pairs_per_expert(L, T) >= MOEQ_GROUPED_WIDE_FROM; }
 
 // IQ2_XXS gate/up for T > 1: the wide kernel (up to four 16-token tiles per decode)
-// from this many pairs per expert
-// (T K / E), the one-tile kernel below it.
+// from this many pairs per expert (T K / E), the one-tile kernel below it.
+// IQ2_XXS + Q2_K at T = 512 / 768 / 1024 / 1536 / 2048 (12 / 18 / 24 / 36 / 48
+// pairs): 1257 / 1768 / 2238 / 3230 / 4201 us with the one-tile kernel against
+// 1687 / 2004 / 2293 / 2877 / 3503 us with the wide one.
 #ifndef MOEQ_IQ2_WIDE_FROM
-#define MOEQ_IQ2_WIDE_FROM 8.0
+#define MOEQ_IQ2_WIDE_FROM 28.0
 #endif
 
 // Q2_K down at T > 1 off the direct path: partials on the block-scaled FP8
